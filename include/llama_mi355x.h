@@ -1,0 +1,166 @@
+/*
+ * llama_mi355x.h -- C ABI of the MI355X (gfx950) Llama-3 decoder forward pass.
+ *
+ * The library computes the decoder stack described in the article "250 lines of code to
+ * build Llama 3 from scratch" (ai02.cc, a walk-through of naklecha/llama3-from-scratch):
+ * token embedding (section 分词器与编码), per layer RMSNorm, Q/K/V projections with
+ * rotary position embedding (sections 查询向量, 位置编码, 键向量, 值向量), causal
+ * grouped-query attention (sections 查询和键相乘, 掩码, 注意力向量, 多头注意力), the
+ * output projection and residual add (section 相加与归一化), the SwiGLU feed-forward
+ * and residual add (section 前馈神经网络层), then the final RMSNorm, the vocabulary
+ * projection and the greedy argmax (section 预测下一个输出).  Prefill runs a whole prompt;
+ * decode runs one token per sequence against a key/value cache pre-allocated by
+ * max_seq x max_batch (the cache sizing described on the Hacker News thread "Llama 3
+ * implemented in pure NumPy").
+ *
+ * Conventions for every entry point
+ *  - All tensor arguments are DEVICE pointers owned by the caller; the library only
+ *    borrows them.  Weights, KV cache and workspace passed to llama_init_weights must stay
+ *    valid until llama_free.  The library allocates no device memory.
+ *  - Matrices are row-major.  Weights are stored [out_features, in_features] and applied
+ *    as x @ W^T, as in the checkpoint (article, section 查询向量).  Q rows are ordered
+ *    head * head_dim + i; K and V rows kv_head * head_dim + i.
+ *  - Weight element type is the config's dtype: LLAMA_BF16 (bfloat16 weights, KV cache and
+ *    GEMM operands, fp32 accumulation, fp32 residual stream and logits) or LLAMA_F32
+ *    (every tensor fp32; the debug/reference precision).  Residual-stream tensors
+ *    (x_in/x_out) and logits are always fp32; token ids are int32.
+ *  - Calls are asynchronous on the given HIP stream (NULL = the null stream).  The library
+ *    never synchronises the device except in llama_sync_status.  One model handle must not
+ *    be used by two host threads at once, nor by overlapping calls on different streams.
+ *  - Every argument, shape and capacity check runs before any device work; on a non-OK
+ *    status nothing has been launched, except for LLAMA_ERR_HIP, which reports a failed
+ *    launch.  A thread-local message describing the last failure is kept
+ *    (llama_last_error).  Cache positions below the call's start position are never
+ *    written.
+ */
+#ifndef LLAMA_MI355X_H
+#define LLAMA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LLAMA_OK = 0,
+    LLAMA_ERR_INVALID_ARG = -1, /* null pointer, out-of-range layer, bad token id (device) */
+    LLAMA_ERR_SHAPE = -2,       /* inconsistent config or call shape                      */
+    LLAMA_ERR_CAPACITY = -3,    /* batch, sequence, token count or buffer size too large   */
+    LLAMA_ERR_DTYPE = -4,       /* unknown dtype                                           */
+    LLAMA_ERR_HIP = -5,         /* a HIP launch or runtime call failed                     */
+    LLAMA_ERR_ALLOC = -6        /* host allocation of the handle failed                    */
+} llama_status;
+
+typedef enum { LLAMA_BF16 = 0, LLAMA_F32 = 1 } llama_dtype;
+
+/* Model hyper-parameters (article, section 下载并读取模型权重: dim 4096, n_layers 32,
+ * n_heads 32, n_kv_heads 8, vocab 128256, norm_eps 1e-5, rope_theta 500000) and the
+ * capacity the caller provisions. */
+typedef struct {
+    int32_t dim;         /* model width D = n_heads * head_dim                              */
+    int32_t n_layers;    /* L                                                               */
+    int32_t n_heads;     /* query heads H                                                   */
+    int32_t n_kv_heads;  /* key/value heads G; H % G == 0; query head h uses KV head h/(H/G) */
+    int32_t head_dim;    /* d, even, <= 256                                                  */
+    int32_t ffn_hidden;  /* SwiGLU hidden width F (14336 for the 8B shape)                   */
+    int32_t vocab_size;  /* V                                                                */
+    float norm_eps;      /* RMSNorm epsilon                                                  */
+    float rope_theta;    /* RoPE base: theta_i = rope_theta^(-2i/d)                          */
+    int32_t max_batch;   /* sequences held in the KV cache                                   */
+    int32_t max_seq;     /* positions held per sequence (pos + S <= max_seq)                  */
+    int32_t max_tokens;  /* largest B*S of one prefill or layer call                          */
+    llama_dtype dtype;   /* weight / cache / operand element type                            */
+} llama_config;
+
+/* Device pointers to one layer's weights, names as in the checkpoint
+ * (layers.N.attention_norm.weight, layers.N.attention.wq.weight, ...). */
+typedef struct {
+    const void *attention_norm; /* [D]                          */
+    const void *wq;             /* [H*d, D]                     */
+    const void *wk;             /* [G*d, D]                     */
+    const void *wv;             /* [G*d, D]                     */
+    const void *wo;             /* [D, H*d]                     */
+    const void *ffn_norm;       /* [D]                          */
+    const void *w1;             /* [F, D]  gate                  */
+    const void *w3;             /* [F, D]  up                    */
+    const void *w2;             /* [D, F]  down                  */
+} llama_layer_weights;
+
+typedef struct {
+    const void *tok_embeddings;        /* [V, D]                                       */
+    const llama_layer_weights *layers; /* HOST array of n_layers entries (copied)      */
+    const void *norm;                  /* [D] final RMSNorm weight                      */
+    const void *output;                /* [V, D] vocabulary projection (not tied)      */
+} llama_weights;
+
+typedef struct llama_model llama_model; /* opaque handle */
+
+/* Bytes of KV cache the caller must provide for this config (layout is internal). */
+size_t llama_kv_cache_bytes(const llama_config *cfg);
+
+/* Bytes of device workspace the caller must provide for this config (activations of up
+ * to max_tokens rows, attention partials, the RoPE table, device flags). */
+size_t llama_workspace_bytes(const llama_config *cfg);
+
+/* Validate cfg, borrow the weights, KV cache and workspace, and return a handle in *out.
+ * Makes no device call; the RoPE table (cos and sin of m*theta_i for every position m <
+ * max_seq, angles formed in double precision, article section 位置编码) is built on the
+ * device by the first call that needs it.  kv_bytes and ws_bytes must be at least the
+ * sizes above, and both buffers 256-byte aligned.  Errors: INVALID_ARG (null pointers),
+ * SHAPE (dim != n_heads*head_dim, H % G != 0, odd or >256 head_dim, non-positive sizes,
+ * bf16 dims that are not multiples of 64), DTYPE, CAPACITY (buffers too small), ALLOC. */
+llama_status llama_init_weights(const llama_config *cfg, const llama_weights *weights,
+                                void *kv_cache, size_t kv_bytes,
+                                void *workspace, size_t ws_bytes, llama_model **out);
+
+/* Causal prefill of B independent sequences of S tokens each, starting at position 0:
+ * embeds tokens [B,S], runs every layer (writing the KV cache at positions 0..S-1 of
+ * sequences 0..B-1), applies the final RMSNorm and the vocabulary projection.  Writes fp32
+ * logits [B,V] of each sequence's last position, or [B,S,V] of every position when
+ * all_positions != 0.  Needs B <= max_batch, S <= max_seq, B*S <= max_tokens. */
+llama_status llama_prefill(llama_model *m, const int32_t *tokens, int32_t B, int32_t S,
+                           float *logits, int32_t all_positions, hipStream_t stream);
+
+/* One KV-cache decode step: token tokens[b] of sequence b sits at position pos, its key
+ * and value are written to the cache at pos, and it attends to cache positions 0..pos.
+ * Writes next_tokens[b] = argmax of its logits (lowest index on ties) and, if logits is
+ * not NULL, the fp32 logits [B,V].  Needs B <= max_batch, 0 <= pos < max_seq, and the
+ * cache filled at 0..pos-1 by earlier calls.  tokens and next_tokens may alias. */
+llama_status llama_decode_step(llama_model *m, const int32_t *tokens, int32_t B, int32_t pos,
+                               float *logits, int32_t *next_tokens, hipStream_t stream);
+
+/* n_steps greedy decode steps starting with tokens[b] at position pos: step k runs at
+ * position pos+k on the previous step's argmax, entirely on the device (the step is
+ * captured once into a HIP graph and replayed).  Writes out_tokens[k*B + b], the argmax
+ * of step k; if logits is not NULL also the logits [n_steps,B,V].  Needs
+ * pos + n_steps <= max_seq. */
+llama_status llama_generate(llama_model *m, const int32_t *tokens, int32_t B, int32_t pos,
+                            int32_t n_steps, int32_t *out_tokens, float *logits,
+                            hipStream_t stream);
+
+/* One decoder layer on hidden states x_in [B,S,D] (fp32) of B sequences whose S tokens sit
+ * at positions start_pos..start_pos+S-1; writes x_out [B,S,D] (may equal x_in) and the
+ * layer's KV cache at those positions, attending to cache positions 0..start_pos+S-1.
+ * With start_pos > 0 the cache must hold positions 0..start_pos-1 (chunked prefill). */
+llama_status llama_layer_forward(llama_model *m, int32_t layer, const float *x_in,
+                                 float *x_out, int32_t B, int32_t S, int32_t start_pos,
+                                 hipStream_t stream);
+
+/* Synchronise the stream, then report device-detected input errors since the last check
+ * (token ids outside [0,V) give INVALID_ARG; their embedding rows are zero; NaN logits in
+ * argmax give INVALID_ARG) and clear them. */
+llama_status llama_sync_status(llama_model *m, hipStream_t stream);
+
+/* Release the handle (the caller's buffers are untouched).  NULL is a no-op. */
+void llama_free(llama_model *m);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *llama_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLAMA_MI355X_H */

@@ -1,0 +1,399 @@
+// The C ABI: validation, buffer carving and the launch sequence of prefill, decode and the
+// single-layer call.  No device memory is allocated here; every buffer is the caller's.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "llama_mi355x.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+llama_status fail(llama_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+
+int seq_stride_of(const llama_config& c) { return (int)align_up((size_t)c.max_seq, 64); }
+size_t elem_size(const llama_config& c) { return c.dtype == LLAMA_BF16 ? 2 : 4; }
+
+// Workspace regions, in order, each 256-byte aligned.
+struct Layout {
+    size_t flags, rope, x, h, q, attn, g, logits, partials, tokbuf, total;
+};
+
+constexpr int kDecodeChunk = 64;  // key positions per split of the decode attention
+
+Layout layout_of(const llama_config& c) {
+    const size_t es = elem_size(c);
+    const size_t rows = (size_t)std::max(c.max_tokens, c.max_batch);
+    const size_t D = c.dim, HD = (size_t)c.n_heads * c.head_dim;
+    const size_t splits = (size_t)seq_stride_of(c) / kDecodeChunk;
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+    L.flags = take(256);
+    L.rope = take((size_t)c.max_seq * (c.head_dim / 2) * sizeof(float2));
+    L.x = take(rows * D * 4);
+    L.h = take(rows * D * es);
+    L.q = take(rows * HD * es);
+    L.attn = take(rows * HD * es);
+    L.g = take(rows * (size_t)c.ffn_hidden * es);
+    L.logits = take((size_t)c.max_batch * c.vocab_size * 4);
+    L.partials = take((size_t)c.max_batch * c.n_heads * splits * (c.head_dim + 2) * 4);
+    L.tokbuf = take((size_t)c.max_batch * 4);
+    L.total = off;
+    return L;
+}
+
+llama_status validate_config(const llama_config* c) {
+    if (!c) return fail(LLAMA_ERR_INVALID_ARG, "config is NULL");
+    if (c->dtype != LLAMA_BF16 && c->dtype != LLAMA_F32)
+        return fail(LLAMA_ERR_DTYPE, "unknown dtype %d", (int)c->dtype);
+    if (c->dim <= 0 || c->n_layers <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 ||
+        c->head_dim <= 0 || c->ffn_hidden <= 0 || c->vocab_size <= 0)
+        return fail(LLAMA_ERR_SHAPE, "model sizes must be positive");
+    if (c->max_batch <= 0 || c->max_seq <= 0 || c->max_tokens <= 0)
+        return fail(LLAMA_ERR_SHAPE, "max_batch, max_seq and max_tokens must be positive");
+    if (c->n_heads % c->n_kv_heads != 0)
+        return fail(LLAMA_ERR_SHAPE, "n_heads %d is not a multiple of n_kv_heads %d", c->n_heads, c->n_kv_heads);
+    if ((long long)c->n_heads * c->head_dim != c->dim)
+        return fail(LLAMA_ERR_SHAPE, "dim %d != n_heads %d * head_dim %d", c->dim, c->n_heads, c->head_dim);
+    if (c->head_dim % 4 != 0 || c->head_dim > 256)
+        return fail(LLAMA_ERR_SHAPE, "head_dim %d must be a multiple of 4 and <= 256", c->head_dim);
+    if (!(c->norm_eps >= 0.0f) || !(c->rope_theta > 0.0f))
+        return fail(LLAMA_ERR_SHAPE, "norm_eps must be >= 0 and rope_theta > 0");
+    if (c->dim % 8 != 0 || c->ffn_hidden % 4 != 0 || c->vocab_size % 4 != 0)
+        return fail(LLAMA_ERR_SHAPE, "dim must be a multiple of 8, ffn_hidden and vocab_size of 4");
+    if (c->dtype == LLAMA_BF16 && (c->dim % 64 || c->ffn_hidden % 64 || c->vocab_size % 64))
+        return fail(LLAMA_ERR_SHAPE, "bf16 needs dim, ffn_hidden and vocab_size multiples of 64");
+    if (c->dim > 16384)
+        return fail(LLAMA_ERR_SHAPE, "dim %d above 16384", c->dim);
+    const long long rows = std::max(c->max_tokens, c->max_batch);
+    if (rows * std::max(c->ffn_hidden, c->vocab_size) >= (1LL << 40))
+        return fail(LLAMA_ERR_CAPACITY, "max_tokens too large");
+    return LLAMA_OK;
+}
+
+}  // namespace
+
+struct llama_model {
+    llama_config cfg;
+    std::vector<llama_layer_weights> layers;
+    const void* tok_embeddings = nullptr;
+    const void* norm = nullptr;
+    const void* output = nullptr;
+    char* kv = nullptr;
+    char* ws = nullptr;
+    Layout L{};
+    lk::Dt dt = lk::Dt::BF16;
+    size_t es = 2;
+    int seq_stride = 0;
+    bool rope_ready = false;
+    // decode-loop graph
+    hipStream_t capture_stream = nullptr;
+    hipGraphExec_t graph_exec = nullptr;
+    int graph_B = -1, graph_max_ctx = -1;
+    int32_t* graph_out = nullptr;
+
+    uint32_t* deverr() { return reinterpret_cast<uint32_t*>(ws + L.flags); }
+    int* pos_ctr() { return reinterpret_cast<int*>(ws + L.flags + 64); }
+    int* step_ctr() { return reinterpret_cast<int*>(ws + L.flags + 128); }
+    float2* rope() { return reinterpret_cast<float2*>(ws + L.rope); }
+    float* x() { return reinterpret_cast<float*>(ws + L.x); }
+    void* h() { return ws + L.h; }
+    void* q() { return ws + L.q; }
+    void* attn() { return ws + L.attn; }
+    void* g() { return ws + L.g; }
+    float* logits_scratch() { return reinterpret_cast<float*>(ws + L.logits); }
+    float* partials() { return reinterpret_cast<float*>(ws + L.partials); }
+    int* tokbuf() { return reinterpret_cast<int*>(ws + L.tokbuf); }
+    size_t kv_layer_elems() const {
+        return (size_t)cfg.max_batch * cfg.n_kv_heads * seq_stride * cfg.head_dim;
+    }
+    char* kc(int l) { return kv + (size_t)l * 2 * kv_layer_elems() * es; }
+    char* vc(int l) { return kc(l) + kv_layer_elems() * es; }
+};
+
+namespace {
+
+#define HIP_TRY(expr)                                                                       \
+    do {                                                                                    \
+        hipError_t e_ = (expr);                                                             \
+        if (e_ != hipSuccess) return fail(LLAMA_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+llama_status ensure_rope(llama_model* m, hipStream_t s) {
+    if (m->rope_ready) return LLAMA_OK;
+    HIP_TRY(lk::zero_u32(m->deverr(), 64, s));  // device flags and counters (first 256 bytes)
+    HIP_TRY(lk::rope_table(m->rope(), m->cfg.max_seq, m->cfg.head_dim, m->cfg.rope_theta, s));
+    m->rope_ready = true;
+    return LLAMA_OK;
+}
+
+lk::GemmArgs<void> gemm_args(const void* A, int lda, const void* w, int M, int N, int K) {
+    lk::GemmArgs<void> g{};
+    g.A = A; g.lda = lda;
+    g.W = WeightRows<void>{w, w, w, N, N, K};
+    g.W3 = g.W;
+    g.M = M; g.N = N; g.K = K;
+    return g;
+}
+
+// One decoder layer on rows = B*S tokens (article, sections 构建Transformer层 to 前馈神经网络层).
+llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int B, int S,
+                       int start_pos, const int* pos_dev, int max_ctx, bool decode,
+                       hipStream_t s) {
+    const llama_config& c = m->cfg;
+    const llama_layer_weights& w = m->layers[l];
+    const int T = B * S, D = c.dim, H = c.n_heads, G = c.n_kv_heads, d = c.head_dim;
+    const int Nq = H * d, Nk = G * d;
+
+    HIP_TRY(lk::rmsnorm(m->dt, xin, 1, 0, w.attention_norm, m->h(), T, D, c.norm_eps, s));
+
+    lk::GemmArgs<void> qkv = gemm_args(m->h(), D, w.wq, T, Nq + 2 * Nk, D);
+    qkv.W = WeightRows<void>{w.wq, w.wk, w.wv, Nq, Nq + Nk, D};
+    EpiQKV<void> eq{m->q(), m->kc(l), m->vc(l), m->rope(), Nq, Nk, d, S, start_pos, G,
+                    m->seq_stride, pos_dev};
+    HIP_TRY(lk::gemm_qkv(m->dt, qkv, eq, s));
+
+    lk::AttnArgs aa{m->q(), m->kc(l), m->vc(l), m->attn(), B, S, start_pos, H, G, d,
+                    m->seq_stride, pos_dev, m->partials(), max_ctx};
+    if (decode) HIP_TRY(lk::attention_decode(m->dt, aa, s));
+    else HIP_TRY(lk::attention_prefill(m->dt, aa, s));
+
+    HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m->attn(), Nq, w.wo, T, D, Nq),
+                              EpiResidual{xin, xout, D}, s));
+    HIP_TRY(lk::rmsnorm(m->dt, xout, 1, 0, w.ffn_norm, m->h(), T, D, c.norm_eps, s));
+    lk::GemmArgs<void> ff = gemm_args(m->h(), D, w.w1, T, c.ffn_hidden, D);
+    ff.W3 = WeightRows<void>{w.w3, w.w3, w.w3, c.ffn_hidden, c.ffn_hidden, D};
+    HIP_TRY(lk::gemm_swiglu(m->dt, ff, m->g(), c.ffn_hidden, s));
+    HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m->g(), c.ffn_hidden, w.w2, T, D, c.ffn_hidden),
+                              EpiResidual{xout, xout, D}, s));
+    return LLAMA_OK;
+}
+
+// Final RMSNorm and vocabulary projection of `rows` rows of x taken every `step` rows
+// starting at `offset` (article, section 预测下一个输出).
+llama_status run_head(llama_model* m, int rows, int step, int offset, float* logits, hipStream_t s) {
+    const llama_config& c = m->cfg;
+    HIP_TRY(lk::rmsnorm(m->dt, m->x(), step, offset, m->norm, m->h(), rows, c.dim, c.norm_eps, s));
+    HIP_TRY(lk::gemm_store_f32(m->dt, gemm_args(m->h(), c.dim, m->output, rows, c.vocab_size, c.dim),
+                               EpiStoreF32{logits, c.vocab_size}, s));
+    return LLAMA_OK;
+}
+
+// One decode step of B rows; position from `pos` or, if pos_dev is set, from device memory.
+llama_status run_decode_step(llama_model* m, const int32_t* tokens, int B, int pos,
+                             const int* pos_dev, int max_ctx, float* logits, int32_t* next,
+                             int32_t* log_out, const int* step_ctr, hipStream_t s) {
+    const llama_config& c = m->cfg;
+    HIP_TRY(lk::embed(m->dt, tokens, m->tok_embeddings, m->x(), B, c.dim, c.vocab_size, m->deverr(), s));
+    for (int l = 0; l < c.n_layers; ++l) {
+        llama_status st = run_layer(m, l, m->x(), m->x(), B, 1, pos, pos_dev, max_ctx, true, s);
+        if (st != LLAMA_OK) return st;
+    }
+    float* lg = logits ? logits : m->logits_scratch();
+    llama_status st = run_head(m, B, 1, 0, lg, s);
+    if (st != LLAMA_OK) return st;
+    HIP_TRY(lk::argmax(lg, B, c.vocab_size, next, log_out, B, step_ctr, m->deverr(), s));
+    return LLAMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t llama_kv_cache_bytes(const llama_config* cfg) {
+    if (validate_config(cfg) != LLAMA_OK) return 0;
+    return (size_t)cfg->n_layers * 2 * cfg->max_batch * cfg->n_kv_heads *
+           (size_t)seq_stride_of(*cfg) * cfg->head_dim * elem_size(*cfg);
+}
+
+size_t llama_workspace_bytes(const llama_config* cfg) {
+    if (validate_config(cfg) != LLAMA_OK) return 0;
+    return layout_of(*cfg).total;
+}
+
+llama_status llama_init_weights(const llama_config* cfg, const llama_weights* w, void* kv_cache,
+                                size_t kv_bytes, void* workspace, size_t ws_bytes,
+                                llama_model** out) {
+    if (!out) return fail(LLAMA_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    llama_status st = validate_config(cfg);
+    if (st != LLAMA_OK) return st;
+    if (!w || !w->tok_embeddings || !w->layers || !w->norm || !w->output)
+        return fail(LLAMA_ERR_INVALID_ARG, "weights struct or one of its pointers is NULL");
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const llama_layer_weights& lw = w->layers[l];
+        if (!lw.attention_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm ||
+            !lw.w1 || !lw.w3 || !lw.w2)
+            return fail(LLAMA_ERR_INVALID_ARG, "layer %d has a NULL weight pointer", l);
+    }
+    if (!kv_cache || !workspace) return fail(LLAMA_ERR_INVALID_ARG, "kv_cache or workspace is NULL");
+    if (((uintptr_t)kv_cache % kAlign) || ((uintptr_t)workspace % kAlign))
+        return fail(LLAMA_ERR_INVALID_ARG, "kv_cache and workspace must be 256-byte aligned");
+    if (kv_bytes < llama_kv_cache_bytes(cfg))
+        return fail(LLAMA_ERR_CAPACITY, "kv_cache has %zu bytes, needs %zu", kv_bytes, llama_kv_cache_bytes(cfg));
+    if (ws_bytes < llama_workspace_bytes(cfg))
+        return fail(LLAMA_ERR_CAPACITY, "workspace has %zu bytes, needs %zu", ws_bytes, llama_workspace_bytes(cfg));
+    llama_model* m = new (std::nothrow) llama_model();
+    if (!m) return fail(LLAMA_ERR_ALLOC, "handle allocation failed");
+    m->cfg = *cfg;
+    m->layers.assign(w->layers, w->layers + cfg->n_layers);
+    m->tok_embeddings = w->tok_embeddings;
+    m->norm = w->norm;
+    m->output = w->output;
+    m->kv = static_cast<char*>(kv_cache);
+    m->ws = static_cast<char*>(workspace);
+    m->L = layout_of(*cfg);
+    m->dt = cfg->dtype == LLAMA_BF16 ? lk::Dt::BF16 : lk::Dt::F32;
+    m->es = elem_size(*cfg);
+    m->seq_stride = seq_stride_of(*cfg);
+    *out = m;
+    return LLAMA_OK;
+}
+
+llama_status llama_prefill(llama_model* m, const int32_t* tokens, int32_t B, int32_t S,
+                           float* logits, int32_t all_positions, hipStream_t s) {
+    if (!m || !tokens || !logits) return fail(LLAMA_ERR_INVALID_ARG, "NULL model, tokens or logits");
+    const llama_config& c = m->cfg;
+    if (B <= 0 || S <= 0) return fail(LLAMA_ERR_SHAPE, "B and S must be positive (B=%d S=%d)", B, S);
+    if (B > c.max_batch) return fail(LLAMA_ERR_CAPACITY, "B=%d > max_batch=%d", B, c.max_batch);
+    if (S > c.max_seq) return fail(LLAMA_ERR_CAPACITY, "S=%d > max_seq=%d", S, c.max_seq);
+    if ((long long)B * S > c.max_tokens)
+        return fail(LLAMA_ERR_CAPACITY, "B*S=%lld > max_tokens=%d", (long long)B * S, c.max_tokens);
+    llama_status st = ensure_rope(m, s);
+    if (st != LLAMA_OK) return st;
+    const int T = B * S;
+    HIP_TRY(lk::embed(m->dt, tokens, m->tok_embeddings, m->x(), T, c.dim, c.vocab_size, m->deverr(), s));
+    for (int l = 0; l < c.n_layers; ++l) {
+        st = run_layer(m, l, m->x(), m->x(), B, S, 0, nullptr, S, false, s);
+        if (st != LLAMA_OK) return st;
+    }
+    if (all_positions) return run_head(m, T, 1, 0, logits, s);
+    return run_head(m, B, S, S - 1, logits, s);
+}
+
+llama_status llama_decode_step(llama_model* m, const int32_t* tokens, int32_t B, int32_t pos,
+                               float* logits, int32_t* next_tokens, hipStream_t s) {
+    if (!m || !tokens || !next_tokens) return fail(LLAMA_ERR_INVALID_ARG, "NULL model, tokens or next_tokens");
+    const llama_config& c = m->cfg;
+    if (B <= 0) return fail(LLAMA_ERR_SHAPE, "B must be positive (B=%d)", B);
+    if (B > c.max_batch) return fail(LLAMA_ERR_CAPACITY, "B=%d > max_batch=%d", B, c.max_batch);
+    if (pos < 0 || pos >= c.max_seq) return fail(LLAMA_ERR_CAPACITY, "pos=%d outside [0, max_seq=%d)", pos, c.max_seq);
+    llama_status st = ensure_rope(m, s);
+    if (st != LLAMA_OK) return st;
+    return run_decode_step(m, tokens, B, pos, nullptr, pos + 1, logits, next_tokens, nullptr, nullptr, s);
+}
+
+llama_status llama_generate(llama_model* m, const int32_t* tokens, int32_t B, int32_t pos,
+                            int32_t n_steps, int32_t* out_tokens, float* logits, hipStream_t s) {
+    if (!m || !tokens || !out_tokens) return fail(LLAMA_ERR_INVALID_ARG, "NULL model, tokens or out_tokens");
+    const llama_config& c = m->cfg;
+    if (B <= 0 || n_steps < 0) return fail(LLAMA_ERR_SHAPE, "B must be positive and n_steps >= 0");
+    if (B > c.max_batch) return fail(LLAMA_ERR_CAPACITY, "B=%d > max_batch=%d", B, c.max_batch);
+    if (pos < 0 || (long long)pos + n_steps > c.max_seq)
+        return fail(LLAMA_ERR_CAPACITY, "pos=%d + n_steps=%d exceeds max_seq=%d", pos, n_steps, c.max_seq);
+    if (n_steps == 0) return LLAMA_OK;
+    llama_status st = ensure_rope(m, s);
+    if (st != LLAMA_OK) return st;
+    const int max_ctx = pos + n_steps;
+    HIP_TRY(lk::copy_tokens(tokens, m->tokbuf(), B, s));
+    HIP_TRY(lk::set_counters(m->pos_ctr(), pos, m->step_ctr(), s));
+    if (logits) {
+        // logits of every step requested: run the steps eagerly, one logits slice each
+        for (int k = 0; k < n_steps; ++k) {
+            st = run_decode_step(m, m->tokbuf(), B, 0, m->pos_ctr(), max_ctx,
+                                 logits + (size_t)k * B * c.vocab_size, m->tokbuf(), out_tokens,
+                                 m->step_ctr(), s);
+            if (st != LLAMA_OK) return st;
+            HIP_TRY(lk::bump_counters(m->pos_ctr(), m->step_ctr(), s));
+        }
+        return LLAMA_OK;
+    }
+    // capture one position-independent step (position and step index live in device memory)
+    if (!m->graph_exec || m->graph_B != B || m->graph_max_ctx < max_ctx || m->graph_out != out_tokens) {
+        if (m->graph_exec) { (void)hipGraphExecDestroy(m->graph_exec); m->graph_exec = nullptr; }
+        if (!m->capture_stream) HIP_TRY(hipStreamCreateWithFlags(&m->capture_stream, hipStreamNonBlocking));
+        const int cap_ctx = std::max(max_ctx, std::min(c.max_seq, max_ctx + 256));
+        HIP_TRY(hipStreamBeginCapture(m->capture_stream, hipStreamCaptureModeThreadLocal));
+        st = run_decode_step(m, m->tokbuf(), B, 0, m->pos_ctr(), cap_ctx, nullptr, m->tokbuf(),
+                             out_tokens, m->step_ctr(), m->capture_stream);
+        hipError_t be = lk::bump_counters(m->pos_ctr(), m->step_ctr(), m->capture_stream);
+        hipGraph_t graph = nullptr;
+        hipError_t ee = hipStreamEndCapture(m->capture_stream, &graph);
+        if (st != LLAMA_OK) { if (graph) (void)hipGraphDestroy(graph); return st; }
+        if (be != hipSuccess || ee != hipSuccess) {
+            if (graph) (void)hipGraphDestroy(graph);
+            return fail(LLAMA_ERR_HIP, "decode graph capture failed: %s",
+                        hipGetErrorString(be != hipSuccess ? be : ee));
+        }
+        hipError_t ie = hipGraphInstantiate(&m->graph_exec, graph, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(graph);
+        if (ie != hipSuccess) { m->graph_exec = nullptr; return fail(LLAMA_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ie)); }
+        m->graph_B = B;
+        m->graph_max_ctx = cap_ctx;
+        m->graph_out = out_tokens;
+    }
+    for (int k = 0; k < n_steps; ++k) HIP_TRY(hipGraphLaunch(m->graph_exec, s));
+    return LLAMA_OK;
+}
+
+llama_status llama_layer_forward(llama_model* m, int32_t layer, const float* x_in, float* x_out,
+                                 int32_t B, int32_t S, int32_t start_pos, hipStream_t s) {
+    if (!m || !x_in || !x_out) return fail(LLAMA_ERR_INVALID_ARG, "NULL model, x_in or x_out");
+    const llama_config& c = m->cfg;
+    if (layer < 0 || layer >= c.n_layers)
+        return fail(LLAMA_ERR_INVALID_ARG, "layer %d outside [0, %d)", layer, c.n_layers);
+    if (B <= 0 || S <= 0) return fail(LLAMA_ERR_SHAPE, "B and S must be positive (B=%d S=%d)", B, S);
+    if (B > c.max_batch) return fail(LLAMA_ERR_CAPACITY, "B=%d > max_batch=%d", B, c.max_batch);
+    if (start_pos < 0 || (long long)start_pos + S > c.max_seq)
+        return fail(LLAMA_ERR_CAPACITY, "start_pos=%d + S=%d exceeds max_seq=%d", start_pos, S, c.max_seq);
+    if ((long long)B * S > c.max_tokens)
+        return fail(LLAMA_ERR_CAPACITY, "B*S=%lld > max_tokens=%d", (long long)B * S, c.max_tokens);
+    llama_status st = ensure_rope(m, s);
+    if (st != LLAMA_OK) return st;
+    return run_layer(m, layer, x_in, x_out, B, S, start_pos, nullptr, start_pos + S, false, s);
+}
+
+llama_status llama_sync_status(llama_model* m, hipStream_t s) {
+    if (!m) return fail(LLAMA_ERR_INVALID_ARG, "NULL model");
+    HIP_TRY(hipStreamSynchronize(s));
+    uint32_t flags = 0;
+    HIP_TRY(hipMemcpy(&flags, m->deverr(), sizeof flags, hipMemcpyDeviceToHost));
+    if (flags) {
+        HIP_TRY(hipMemset(m->deverr(), 0, sizeof flags));
+        HIP_TRY(hipDeviceSynchronize());
+        return fail(LLAMA_ERR_INVALID_ARG, "device reported %s%s",
+                    (flags & DEVERR_TOKEN_RANGE) ? "token id outside [0, vocab) " : "",
+                    (flags & DEVERR_NAN_LOGIT) ? "NaN logits" : "");
+    }
+    return LLAMA_OK;
+}
+
+void llama_free(llama_model* m) {
+    if (!m) return;
+    if (m->graph_exec) (void)hipGraphExecDestroy(m->graph_exec);
+    if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
+    delete m;
+}
+
+const char* llama_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+// Embedding gather, RMSNorm, RoPE table, argmax and small device-counter kernels.
+#include "launch.hpp"
+
+namespace lk {
+
+// cos and sin of pos * theta_i, theta_i = theta^(-i/(d/2)); the angle and both functions in
+// double precision, rounded to float (article, section 位置编码).
+__global__ void rope_table_kernel(float2* rope, int max_seq, int half, double theta) {
+    const int pos = blockIdx.x;
+    for (int i = threadIdx.x; i < half; i += blockDim.x) {
+        const double freq = 1.0 / pow(theta, (double)i / (double)half);
+        const double ang = (double)pos * freq;
+        rope[(size_t)pos * half + i] = make_float2((float)cos(ang), (float)sin(ang));
+    }
+}
+
+hipError_t rope_table(float2* rope, int max_seq, int d, float theta, hipStream_t s) {
+    rope_table_kernel<<<max_seq, 64, 0, s>>>(rope, max_seq, d / 2, (double)theta);
+    return hipGetLastError();
+}
+
+// x[r] = E[tokens[r]] widened to fp32 (article, section 分词器与编码).  Ids outside [0,V)
+// give a zero row and raise DEVERR_TOKEN_RANGE.
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int* tokens, const T* E, float* x,
+                                                    int D, int V, uint32_t* err) {
+    const int r = blockIdx.x;
+    const int tok = tokens[r];
+    float* xr = x + (size_t)r * D;
+    if (tok < 0 || tok >= V) {
+        if (threadIdx.x == 0) atomicOr(err, DEVERR_TOKEN_RANGE);
+        for (int i = threadIdx.x; i < D; i += blockDim.x) xr[i] = 0.0f;
+        return;
+    }
+    const T* er = E + (size_t)tok * D;
+    for (int i = threadIdx.x * 8; i < D; i += blockDim.x * 8) {
+        float v[8];
+        load8(er + i, v);
+        *reinterpret_cast<f32x4*>(xr + i) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(xr + i + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+}
+
+hipError_t embed(Dt dt, const int* tokens, const void* E, float* x, int rows, int D, int V,
+                 uint32_t* err, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    if (dt == Dt::BF16)
+        embed_kernel<bf16><<<rows, 256, 0, s>>>(tokens, (const bf16*)E, x, D, V, err);
+    else
+        embed_kernel<float><<<rows, 256, 0, s>>>(tokens, (const float*)E, x, D, V, err);
+    return hipGetLastError();
+}
+
+// y = x * 1/sqrt(mean(x^2) + eps) * w per row (article, section 分词器与编码; also the
+// pitchhut deep-dive's layer-normalisation example).  One 256-thread block per row; the
+// row lives in registers between the two passes.  D % 8 == 0, D <= 256*8*MAXV.
+template <typename T, int MAXV>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int in_step, int in_off,
+                                                      const T* w, T* y, int D, float eps) {
+    const int r = blockIdx.x;
+    const float* xr = x + ((size_t)r * in_step + in_off) * D;
+    float v[MAXV][8];
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < MAXV; ++c) {
+        const int i = (threadIdx.x + c * 256) * 8;
+        if (i < D) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(xr + i);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(xr + i + 4);
+            v[c][0] = a[0]; v[c][1] = a[1]; v[c][2] = a[2]; v[c][3] = a[3];
+            v[c][4] = b[0]; v[c][5] = b[1]; v[c][6] = b[2]; v[c][7] = b[3];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ss += v[c][j] * v[c][j];
+        }
+    }
+    __shared__ float red[4];
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float total = red[0] + red[1] + red[2] + red[3];
+    const float inv = 1.0f / sqrtf(total / (float)D + eps);
+    T* yr = y + (size_t)r * D;
+#pragma unroll
+    for (int c = 0; c < MAXV; ++c) {
+        const int i = (threadIdx.x + c * 256) * 8;
+        if (i < D) {
+            float wv[8];
+            load8(w + i, wv);
+            float o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = (v[c][j] * inv) * wv[j];
+            store4(yr + i, o);
+            store4(yr + i + 4, o + 4);
+        }
+    }
+}
+
+template <typename T>
+static hipError_t rmsnorm_t(const float* x, int step, int off, const T* w, T* y, int rows, int D,
+                            float eps, hipStream_t s) {
+    if (D <= 2048)
+        rmsnorm_kernel<T, 1><<<rows, 256, 0, s>>>(x, step, off, w, y, D, eps);
+    else if (D <= 4096)
+        rmsnorm_kernel<T, 2><<<rows, 256, 0, s>>>(x, step, off, w, y, D, eps);
+    else if (D <= 8192)
+        rmsnorm_kernel<T, 4><<<rows, 256, 0, s>>>(x, step, off, w, y, D, eps);
+    else
+        rmsnorm_kernel<T, 8><<<rows, 256, 0, s>>>(x, step, off, w, y, D, eps);
+    return hipGetLastError();
+}
+
+hipError_t rmsnorm(Dt dt, const float* x, int in_row_step, int in_row_offset, const void* w,
+                   void* y, int rows, int D, float eps, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    if (dt == Dt::BF16)
+        return rmsnorm_t<bf16>(x, in_row_step, in_row_offset, (const bf16*)w, (bf16*)y, rows, D, eps, s);
+    return rmsnorm_t<float>(x, in_row_step, in_row_offset, (const float*)w, (float*)y, rows, D, eps, s);
+}
+
+// Greedy choice per row: the largest logit, lowest index among equals (article, section
+// 预测下一个输出, torch.argmax).  NaN raises DEVERR_NAN_LOGIT.  Writes out[r]; if out2 is
+// set also out2[(*counter) * out2_step + r] (the generated-token log of a decode loop).
+__global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int V, int* out,
+                                                      int* out2, int out2_step,
+                                                      const int* counter, uint32_t* err) {
+    const int r = blockIdx.x;
+    const float* lr = logits + (size_t)r * V;
+    float best = -INFINITY;
+    int idx = 0x7fffffff;
+    bool nan = false;
+    for (int i = threadIdx.x; i < V; i += blockDim.x) {
+        const float v = lr[i];
+        if (v != v) nan = true;
+        if (v > best || (v == best && i < idx)) { best = v; idx = i; }
+    }
+    // wave reduce
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ob = __shfl_xor(best, o, WAVE);
+        const int oi = __shfl_xor(idx, o, WAVE);
+        if (ob > best || (ob == best && oi < idx)) { best = ob; idx = oi; }
+    }
+    __shared__ float sb[16];
+    __shared__ int si[16];
+    __shared__ int snan;
+    if (threadIdx.x == 0) snan = 0;
+    __syncthreads();
+    if (nan) snan = 1;
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { sb[w] = best; si[w] = idx; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float b = sb[0];
+        int ix = si[0];
+        for (int k = 1; k < (int)(blockDim.x >> 6); ++k)
+            if (sb[k] > b || (sb[k] == b && si[k] < ix)) { b = sb[k]; ix = si[k]; }
+        if (snan) { atomicOr(err, DEVERR_NAN_LOGIT); ix = 0; }
+        if (ix == 0x7fffffff) ix = 0;  // all -inf
+        out[r] = ix;
+        if (out2) out2[(size_t)(*counter) * out2_step + r] = ix;
+    }
+}
+
+hipError_t argmax(const float* logits, int rows, int V, int* out, int* out2, int out2_step,
+                  const int* counter, uint32_t* err, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    argmax_kernel<<<rows, 1024, 0, s>>>(logits, V, out, out2, out2_step, counter, err);
+    return hipGetLastError();
+}
+
+__global__ void bump_counters_kernel(int* pos, int* step) {
+    if (threadIdx.x == 0) { *pos += 1; *step += 1; }
+}
+hipError_t bump_counters(int* pos, int* step, hipStream_t s) {
+    bump_counters_kernel<<<1, 64, 0, s>>>(pos, step);
+    return hipGetLastError();
+}
+
+__global__ void set_counters_kernel(int* pos, int pos_value, int* step) {
+    if (threadIdx.x == 0) { *pos = pos_value; *step = 0; }
+}
+hipError_t set_counters(int* pos, int pos_value, int* step, hipStream_t s) {
+    set_counters_kernel<<<1, 64, 0, s>>>(pos, pos_value, step);
+    return hipGetLastError();
+}
+
+__global__ void zero_u32_kernel(uint32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+hipError_t zero_u32(uint32_t* p, int n, hipStream_t s) {
+    zero_u32_kernel<<<(n + 255) / 256, 256, 0, s>>>(p, n);
+    return hipGetLastError();
+}
+
+__global__ void copy_tokens_kernel(const int* src, int* dst, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src[i];
+}
+hipError_t copy_tokens(const int* src, int* dst, int n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    copy_tokens_kernel<<<(n + 255) / 256, 256, 0, s>>>(src, dst, n);
+    return hipGetLastError();
+}
+
+}  // namespace lk

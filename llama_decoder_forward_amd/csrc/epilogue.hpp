@@ -1,0 +1,92 @@
+// GEMM epilogues.  Every GEMM computes acc[m][n] = sum_k A[m][k] * W[n][k] (token row m,
+// weight row n) in fp32 and hands the result to an epilogue in groups of four consecutive
+// output columns n, n+1, n+2, n+3 (n % 4 == 0) of one row m.
+#pragma once
+#include "common.hpp"
+
+// Weight rows of a GEMM, possibly split over up to three matrices stacked along n
+// (Q, K and V projections share one GEMM: rows [0,end0) of p0, then p1, then p2).
+template <typename T>
+struct WeightRows {
+    const T* p0; const T* p1; const T* p2;
+    int end0, end1;  // cumulative row ends of p0 and p1
+    int ld;          // row stride (= K)
+    __device__ __forceinline__ const T* row(int n) const {
+        if (n < end0) return p0 + (size_t)n * ld;
+        if (n < end1) return p1 + (size_t)(n - end0) * ld;
+        return p2 + (size_t)(n - end1) * ld;
+    }
+};
+
+// logits (or any plain fp32 output): C[m][n] = acc
+struct EpiStoreF32 {
+    float* C; int ldc;
+    __device__ __forceinline__ void operator()(int m, int n, float v[4]) const {
+        store4(C + (size_t)m * ldc + n, v);
+    }
+};
+
+// Residual add into the fp32 hidden state (article, section 相加与归一化 and the add after
+// the feed-forward): xout[m][n] = xin[m][n] + acc.  xin may equal xout.
+struct EpiResidual {
+    const float* xin; float* xout; int ld;
+    __device__ __forceinline__ void operator()(int m, int n, float v[4]) const {
+        const f32x4 r = *reinterpret_cast<const f32x4*>(xin + (size_t)m * ld + n);
+        float o[4] = {r[0] + v[0], r[1] + v[1], r[2] + v[2], r[3] + v[3]};
+        store4(xout + (size_t)m * ld + n, o);
+    }
+};
+
+// SwiGLU gate (article, section 前馈神经网络层): g[m][n] = silu(h.w1_n) * (h.w3_n),
+// silu(z) = z / (1 + exp(-z)).
+template <typename T>
+struct EpiSwiGLU {
+    T* g; int ld;
+    __device__ __forceinline__ void operator()(int m, int n, float gate[4], float up[4]) const {
+        float o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = gate[i] / (1.0f + __expf(-gate[i])) * up[i];
+        store4(g + (size_t)m * ld + n, o);
+    }
+};
+
+// Q/K/V projection epilogue: rotary embedding of q and k (article, section 位置编码:
+// adjacent pairs (x[2i], x[2i+1]) rotated by the angle pos * theta_i), q stored for the
+// attention kernel, k and v written to the KV cache at their positions.
+//   q   : [M][Nq] with Nq = H*d, row m = token (sequence m / S, position start + m % S)
+//   kc  : this layer's K cache [max_batch][G][seq_stride][d]
+//   vc  : this layer's V cache, transposed: [max_batch][G][d][seq_stride]
+//   rope: [max_seq][d/2] of (cos, sin)
+template <typename T>
+struct EpiQKV {
+    T* q; T* kc; T* vc;
+    const float2* rope;
+    int Nq, Nk, d, S, start_pos, G, seq_stride;
+    const int* pos_dev;  // if set, the start position is read from device memory
+
+    __device__ __forceinline__ void operator()(int m, int n, float v[4]) const {
+        const int b = m / S;
+        const int pos = (pos_dev ? *pos_dev : start_pos) + (m - b * S);
+        if (n < Nq + Nk) {
+            const int j = (n < Nq ? n : n - Nq) % d;  // even; pairs (j, j+1), (j+2, j+3)
+            const float2 cs0 = rope[(size_t)pos * (d / 2) + j / 2];
+            const float2 cs1 = rope[(size_t)pos * (d / 2) + j / 2 + 1];
+            const float a0 = v[0], b0 = v[1], a1 = v[2], b1 = v[3];
+            v[0] = a0 * cs0.x - b0 * cs0.y;
+            v[1] = a0 * cs0.y + b0 * cs0.x;
+            v[2] = a1 * cs1.x - b1 * cs1.y;
+            v[3] = a1 * cs1.y + b1 * cs1.x;
+        }
+        if (n < Nq) {
+            store4(q + (size_t)m * Nq + n, v);
+        } else if (n < Nq + Nk) {
+            const int nk = n - Nq, g = nk / d, j = nk - g * d;
+            store4(kc + (((size_t)b * G + g) * seq_stride + pos) * d + j, v);
+        } else {
+            const int nv = n - Nq - Nk, g = nv / d, j = nv - g * d;
+            T* base = vc + (((size_t)b * G + g) * d + j) * seq_stride + pos;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) base[(size_t)i * seq_stride] = from_f32<T>(v[i]);
+        }
+    }
+};

@@ -1,0 +1,50 @@
+// Host-side launchers of the kernels (internal to the library).  Each returns the
+// hipError_t of its launch.  Shapes are validated by the caller (api.hip).
+#pragma once
+#include "epilogue.hpp"
+
+namespace lk {
+
+enum class Dt { BF16, F32 };
+
+// ---- elementwise / reductions (elementwise.hip)
+hipError_t rope_table(float2* rope, int max_seq, int d, float theta, hipStream_t s);
+hipError_t embed(Dt dt, const int* tokens, const void* E, float* x, int rows, int D, int V,
+                 uint32_t* err, hipStream_t s);
+// y[r] = rmsnorm(x[r * in_stride_rows + in_offset_rows]) for r < rows
+hipError_t rmsnorm(Dt dt, const float* x, int in_row_step, int in_row_offset, const void* w,
+                   void* y, int rows, int D, float eps, hipStream_t s);
+hipError_t argmax(const float* logits, int rows, int V, int* out, int* out2, int out2_step,
+                  const int* counter, uint32_t* err, hipStream_t s);
+hipError_t bump_counters(int* pos, int* step, hipStream_t s);
+hipError_t zero_u32(uint32_t* p, int n, hipStream_t s);
+hipError_t copy_tokens(const int* src, int* dst, int n, hipStream_t s);
+hipError_t set_counters(int* pos, int pos_value, int* step, hipStream_t s);
+
+// ---- GEMMs: acc[m][n] = sum_k A[m][k] W[n][k]  (gemm_mfma.hip, gemm_simt.hip, gemm_skinny.hip)
+template <typename T> struct GemmArgs {
+    const T* A; int lda;
+    WeightRows<T> W;
+    WeightRows<T> W3;  // second weight set of the SwiGLU gate/up GEMM
+    int M, N, K;
+};
+hipError_t gemm_store_f32(Dt dt, const GemmArgs<void>& g, EpiStoreF32 e, hipStream_t s);
+hipError_t gemm_residual(Dt dt, const GemmArgs<void>& g, EpiResidual e, hipStream_t s);
+hipError_t gemm_swiglu(Dt dt, const GemmArgs<void>& g, void* out, int ld, hipStream_t s);
+hipError_t gemm_qkv(Dt dt, const GemmArgs<void>& g, const EpiQKV<void>& e, hipStream_t s);
+
+// ---- attention (attention.hip)
+struct AttnArgs {
+    const void* q;   // [rows][H*d], row = b*S + s
+    const void* kc;  // layer K cache
+    const void* vc;  // layer V^T cache
+    void* out;       // [rows][H*d]
+    int B, S, start_pos, H, G, d, seq_stride;
+    const int* pos_dev;
+    float* partials; // decode split-K scratch
+    int max_ctx;     // upper bound of start_pos + S (sizing of decode grids)
+};
+hipError_t attention_prefill(Dt dt, const AttnArgs& a, hipStream_t s);
+hipError_t attention_decode(Dt dt, const AttnArgs& a, hipStream_t s);
+
+}  // namespace lk

@@ -1,0 +1,140 @@
+"""The C ABI on a machine without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments, shapes and capacities before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from llama_decoder_forward_amd import binding as bd
+from llama_decoder_forward_amd import synthetic as syn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llama_mi355x.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.LIB_PATH):
+        from llama_decoder_forward_amd import build
+        build.build()
+    return bd.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(llama_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    declared = _declared_functions()
+    assert set(declared) == set(bd.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _cfg(**over):
+    c = bd.make_config(syn.TINY, max_batch=2, max_seq=32, max_tokens=64)
+    for k, v in over.items():
+        setattr(c, k, v)
+    return c
+
+
+def _init(lib, cfg, kv=0x100000, ws=0x200000, kvb=None, wsb=None, layers_null=False):
+    L = max(cfg.n_layers, 1)
+    layers = (bd.LlamaLayerWeights * L)()
+    for l in range(L):
+        layers[l] = bd.LlamaLayerWeights(*([0x1000] * 9))
+    if layers_null:
+        layers[L - 1].w2 = None
+    w = bd.LlamaWeights(0x1000, layers, 0x1000, 0x1000)
+    if kvb is None:
+        kvb = lib.llama_kv_cache_bytes(ctypes.byref(cfg))
+    if wsb is None:
+        wsb = lib.llama_workspace_bytes(ctypes.byref(cfg))
+    h = ctypes.c_void_p()
+    st = lib.llama_init_weights(ctypes.byref(cfg), ctypes.byref(w), kv, kvb, ws, wsb, ctypes.byref(h))
+    return st, h
+
+
+def test_kv_cache_bytes_matches_documented_layout(lib):
+    c = _cfg()
+    # L * {K, V} * max_batch * G * (max_seq rounded up to 64) * d * 4 bytes (fp32)
+    assert lib.llama_kv_cache_bytes(ctypes.byref(c)) == 2 * 2 * 2 * 2 * 64 * 16 * 4
+    c8 = bd.make_config(syn.LLAMA3_8B, max_batch=32, max_seq=4224, max_tokens=2048)
+    assert lib.llama_kv_cache_bytes(ctypes.byref(c8)) == 32 * 2 * 32 * 8 * 4224 * 128 * 2
+    assert lib.llama_workspace_bytes(ctypes.byref(c8)) > 2048 * 14336 * 2
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_heads", 3, -2),        # H % G != 0 (and dim != H*d)
+    ("head_dim", 15, -2),      # dim != H*d
+    ("dim", 0, -2),
+    ("max_seq", 0, -2),
+    ("dtype", 7, -4),
+    ("rope_theta", -1.0, -2),
+])
+def test_bad_config_rejected(lib, field, value, status):
+    c = _cfg(**{field: value})
+    assert lib.llama_kv_cache_bytes(ctypes.byref(c)) == 0
+    st, h = _init(lib, c, kvb=1 << 30, wsb=1 << 30)
+    assert st == status and not h.value
+    assert lib.llama_last_error().decode() != ""
+
+
+def test_bf16_dims_must_be_multiples_of_64(lib):
+    c = _cfg(dtype=bd.LLAMA_BF16, ffn_hidden=200)
+    st, _ = _init(lib, c, kvb=1 << 30, wsb=1 << 30)
+    assert st == -2
+
+
+def test_init_argument_errors(lib):
+    c = _cfg()
+    assert _init(lib, c, kv=0)[0] == -1
+    assert _init(lib, c, ws=0x200010)[0] == -1            # misaligned workspace
+    assert _init(lib, c, layers_null=True)[0] == -1
+    kvb = lib.llama_kv_cache_bytes(ctypes.byref(c))
+    assert _init(lib, c, kvb=kvb - 1)[0] == -3
+    wsb = lib.llama_workspace_bytes(ctypes.byref(c))
+    assert _init(lib, c, wsb=wsb - 256)[0] == -3
+    h = ctypes.c_void_p()
+    assert lib.llama_init_weights(ctypes.byref(c), None, 0x100000, kvb, 0x200000, wsb, ctypes.byref(h)) == -1
+
+
+@pytest.fixture()
+def handle(lib):
+    st, h = _init(lib, _cfg())   # init touches no device memory
+    assert st == 0 and h.value
+    yield h
+    lib.llama_free(h)
+
+
+def test_call_shape_and_capacity_errors_before_device_work(lib, handle):
+    T = 0x300000
+    assert lib.llama_prefill(handle, T, 3, 4, T, 0, None) == -3         # B > max_batch
+    assert lib.llama_prefill(handle, T, 1, 33, T, 0, None) == -3        # S > max_seq
+    assert lib.llama_prefill(handle, T, 2, 0, T, 0, None) == -2
+    assert lib.llama_prefill(handle, None, 1, 4, T, 0, None) == -1
+    assert lib.llama_decode_step(handle, T, 1, 32, T, T, None) == -3    # pos >= max_seq
+    assert lib.llama_decode_step(handle, T, 1, -1, T, T, None) == -3
+    assert lib.llama_decode_step(handle, T, 0, 3, T, T, None) == -2
+    assert lib.llama_decode_step(handle, T, 1, 3, T, None, None) == -1
+    assert lib.llama_generate(handle, T, 1, 30, 3, T, None, None) == -3  # 30 + 3 > 32
+    assert lib.llama_layer_forward(handle, 2, T, T, 1, 4, 0, None) == -1  # layer out of range
+    assert lib.llama_layer_forward(handle, 0, T, T, 1, 4, 30, None) == -3
+    assert lib.llama_layer_forward(handle, 0, T, T, 3, 1, 0, None) == -3
+    assert "max_batch" in lib.llama_last_error().decode()
+    assert lib.llama_sync_status(None, None) == -1
+
+
+def test_max_tokens_bounds_prefill(lib):
+    c = _cfg(max_tokens=8)
+    st, h = _init(lib, c)
+    assert st == 0
+    assert lib.llama_prefill(h, 0x300000, 2, 5, 0x300000, 0, None) == -3  # 10 > 8
+    lib.llama_free(h)
+
+
+def test_free_null_is_noop(lib):
+    lib.llama_free(None)

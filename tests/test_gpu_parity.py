@@ -1,0 +1,179 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Sizes here finish in seconds on the oracle and still span several GEMM / attention tiles
+and a ragged tail.  bf16 results must be within 2e-2 normwise per row of the oracle
+(float64, fed the exact bf16 weights); the fp32 debug path within 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+from llama_decoder_forward_amd import binding as bd
+from llama_decoder_forward_amd import synthetic as syn
+from oracle import llama_oracle as O
+
+from gpu_util import (BF16_TOL, F32_TOL, assert_rows_close, build_model, check_argmax,
+                      require_gpu, say, small_bf16_spec)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+# ------------------------------------------------------------------ tiny fp32 stack
+
+def test_tiny_fp32_prefill_all_positions():
+    say("tiny fp32 prefill: B=1 S=17")
+    spec = syn.TINY
+    m, synth = build_model(spec, 1, max_batch=1, max_seq=32, max_tokens=32)
+    toks = syn.tokens(1, 1, 17, spec.vocab_size)
+    got = m.prefill(torch.from_numpy(toks).cuda(), all_positions=True).cpu().numpy()
+    ref, _ = O.prefill(toks, syn.FloatView(synth), spec, all_positions=True)
+    assert_rows_close(got, ref, F32_TOL, "tiny prefill logits")
+    last = m.prefill(torch.from_numpy(toks).cuda()).cpu().numpy()
+    np.testing.assert_array_equal(last[0], got[0, -1])
+    m.sync_status()
+
+
+def test_tiny_fp32_greedy_decode_matches_oracle():
+    say("tiny fp32: prefill + 8 greedy decode steps")
+    spec = syn.TINY
+    m, synth = build_model(spec, 1, max_batch=1, max_seq=32, max_tokens=32)
+    toks = syn.tokens(1, 1, 17, spec.vocab_size)
+    l0_ref, ls_ref, chosen_ref = O.greedy_generate(toks, 8, syn.FloatView(synth), spec)
+    l0 = m.prefill(torch.from_numpy(toks).cuda()).cpu().numpy()
+    assert_rows_close(l0, l0_ref, F32_TOL, "prefill logits")
+    cur = torch.tensor(np.argmax(l0, axis=-1).astype(np.int32)).cuda()
+    chosen = [cur.cpu().numpy()]
+    for k in range(8):
+        nxt, lg = m.decode_step(cur, 17 + k)
+        assert_rows_close(lg.cpu().numpy(), ls_ref[k], F32_TOL, f"decode step {k}")
+        chosen.append(nxt.cpu().numpy())
+        cur = nxt
+    np.testing.assert_array_equal(np.stack(chosen), chosen_ref)   # strict at fp32
+    m.sync_status()
+
+
+def test_tiny_fp32_generate_loop_matches_oracle():
+    say("tiny fp32: generate (graph) and generate with logits")
+    spec = syn.TINY
+    m, synth = build_model(spec, 1, max_batch=2, max_seq=40, max_tokens=40)
+    toks = syn.tokens(1, 2, 17, spec.vocab_size)
+    _, ls_ref, chosen_ref = O.greedy_generate(toks, 8, syn.FloatView(synth), spec)
+    l0 = m.prefill(torch.from_numpy(toks).cuda())
+    first = l0.argmax(-1).to(torch.int32).contiguous()
+    out, _ = m.generate(first, 17, 8)
+    np.testing.assert_array_equal(out.cpu().numpy(), chosen_ref[1:])
+    # again with logits (eager steps), after re-prefilling the cache
+    m.prefill(torch.from_numpy(toks).cuda())
+    out2, lg = m.generate(first, 17, 8, want_logits=True)
+    np.testing.assert_array_equal(out2.cpu().numpy(), chosen_ref[1:])
+    assert_rows_close(lg.cpu().numpy(), ls_ref, F32_TOL, "generate logits")
+    # replaying the captured graph a second time gives the same tokens
+    m.prefill(torch.from_numpy(toks).cuda())
+    out3, _ = m.generate(first, 17, 8)
+    np.testing.assert_array_equal(out3.cpu().numpy(), chosen_ref[1:])
+    m.sync_status()
+
+
+# ------------------------------------------------------------------ 8B-shaped layer, S=17
+
+def test_llama3_8b_layer_bf16_seq17():
+    say("8B-shaped layer bf16: B=1 S=17")
+    spec = syn.LLAMA3_8B_ONE_LAYER
+    m, synth = build_model(spec, 2, max_batch=1, max_seq=64, max_tokens=64)
+    x = syn.normal(2, "x", (1, 17, spec.dim))
+    got = m.layer_forward(0, torch.from_numpy(x).cuda()).cpu().numpy()
+    cache = O.SequenceCache(spec, 17)
+    ref = O.layer_forward(x[0].astype(np.float64), syn.FloatView(synth), spec, 0, cache, 0)
+    assert_rows_close(got[0], ref, BF16_TOL, "layer output")
+    k = m.cache_k(0)[0, :, :17].float().cpu().numpy()
+    v = m.cache_v(0)[0, :, :17].float().cpu().numpy()
+    assert_rows_close(k, cache.k[0], BF16_TOL, "K cache")
+    assert_rows_close(v, cache.v[0], BF16_TOL, "V cache")
+
+
+# ------------------------------------------------------------------ small bf16 stack, many tiles
+
+@pytest.mark.parametrize("B,S", [(3, 150), (1, 1), (2, 64)])
+def test_bf16_stack_prefill_all_positions(B, S):
+    say(f"small bf16 stack prefill B={B} S={S}")
+    spec = small_bf16_spec()
+    m, synth = build_model(spec, 3, max_batch=4, max_seq=160, max_tokens=512)
+    toks = syn.tokens(3, B, S, spec.vocab_size)
+    got = m.prefill(torch.from_numpy(toks).cuda(), all_positions=True).cpu().numpy()
+    ref, _ = O.prefill(toks, syn.FloatView(synth), spec, all_positions=True)
+    assert_rows_close(got, ref, BF16_TOL, "prefill logits")
+    m.sync_status()
+
+
+@pytest.mark.parametrize("H,G", [(4, 4), (4, 1)])
+def test_bf16_mha_and_single_kv_head(H, G):
+    say(f"small bf16 stack H={H} G={G}")
+    spec = small_bf16_spec(n_heads=H, n_kv_heads=G)
+    m, synth = build_model(spec, 4, max_batch=2, max_seq=80, max_tokens=160)
+    toks = syn.tokens(4, 2, 70, spec.vocab_size)
+    got = m.prefill(torch.from_numpy(toks).cuda(), all_positions=True).cpu().numpy()
+    ref, _ = O.prefill(toks, syn.FloatView(synth), spec, all_positions=True)
+    assert_rows_close(got, ref, BF16_TOL, "prefill logits")
+
+
+def test_bf16_teacher_forced_decode():
+    say("small bf16 stack: prefill S=100 then 6 teacher-forced decode steps, B=3")
+    spec = small_bf16_spec()
+    B, S, steps = 3, 100, 6
+    m, synth = build_model(spec, 5, max_batch=B, max_seq=128, max_tokens=B * S)
+    toks = syn.tokens(5, B, S, spec.vocab_size)
+    W = syn.FloatView(synth)
+    ref0, caches = O.prefill(toks, W, spec, capacity=S + steps)
+    got0 = m.prefill(torch.from_numpy(toks).cuda()).cpu().numpy()
+    assert_rows_close(got0, ref0, BF16_TOL, "prefill last logits")
+    cur = O.argmax(ref0).astype(np.int32)
+    for k in range(steps):
+        ref = O.decode_step(cur, S + k, W, spec, caches)
+        nxt, lg = m.decode_step(torch.from_numpy(cur).cuda(), S + k)
+        lg = lg.cpu().numpy()
+        assert_rows_close(lg, ref, BF16_TOL, f"decode step {k}")
+        check_argmax(nxt.cpu().numpy(), lg, ref, f"decode step {k}")
+        cur = O.argmax(ref).astype(np.int32)     # teacher forcing: oracle's token
+    m.sync_status()
+
+
+def test_bf16_chunked_layer_forward():
+    say("small bf16 layer: chunked prefill 40 + 37 + 1 tokens")
+    spec = small_bf16_spec(n_layers=1)
+    m, synth = build_model(spec, 6, max_batch=2, max_seq=96, max_tokens=192)
+    x = syn.normal(6, "x", (2, 78, spec.dim))
+    W = syn.FloatView(synth)
+    outs = []
+    for a, b in ((0, 40), (40, 77), (77, 78)):
+        outs.append(m.layer_forward(0, torch.from_numpy(np.ascontiguousarray(x[:, a:b])).cuda(),
+                                    start_pos=a).cpu().numpy())
+    got = np.concatenate(outs, axis=1)
+    for bidx in range(2):
+        cache = O.SequenceCache(spec, 78)
+        ref = O.layer_forward(x[bidx].astype(np.float64), W, spec, 0, cache, 0)
+        assert_rows_close(got[bidx], ref, BF16_TOL, f"chunked layer row {bidx}")
+
+
+def test_prefill_is_deterministic():
+    spec = small_bf16_spec()
+    m, _ = build_model(spec, 7, max_batch=2, max_seq=128, max_tokens=256)
+    toks = torch.from_numpy(syn.tokens(7, 2, 128, spec.vocab_size)).cuda()
+    a = m.prefill(toks, all_positions=True)
+    b = m.prefill(toks, all_positions=True)
+    assert torch.equal(a, b)
+
+
+def test_out_of_range_token_is_reported():
+    spec = syn.TINY
+    m, _ = build_model(spec, 1, max_batch=1, max_seq=16, max_tokens=16)
+    bad = torch.tensor([[1, 2, spec.vocab_size + 5]], dtype=torch.int32).cuda()
+    m.prefill(bad)
+    with pytest.raises(bd.LlamaError) as e:
+        m.sync_status()
+    assert e.value.status == -1
+    m.sync_status()  # cleared
