@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Throughput of the Llama-3-8B-shaped decoder forward on one MI355X.
+
+Headline (``value``): causal prefill tokens/s of one batch-1, 2048-token sequence through
+the 32-layer 8B-shaped stack to the last token's logits (bf16 weights, fp32 accumulation),
+with the step's share of the bf16 dense MFMA peak.  ``decode``: greedy KV-cache decode
+tokens/s for 32 sequences whose caches hold 4096 prefilled positions, 128 steps, with the
+step's share of peak HBM bandwidth.  Inputs are seeded synthetic tensors already resident
+in HBM when timing starts.  ``roofline`` is the prefill's dominant kernel (the W1/W3
+projection with SiLU*up), timed with HIP events on the launch stream during the timed
+steps.  ``cpu_baseline`` times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "prefill tokens/s (%MFMA peak) + decode tokens/s (%HBM BW), 8B-shape, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_flops(spec, B: int, S: int) -> float:
+    """Algorithmic FLOPs of one prefill: layer GEMMs for every token, the causal lower
+    triangle of attention, and the vocabulary projection of the last token."""
+    D, H, G, d, F = spec.dim, spec.n_heads, spec.n_kv_heads, spec.head_dim, spec.ffn_hidden
+    per_tok = 2 * (D * (H + 2 * G) * d + H * d * D + 3 * D * F)
+    attn = 4 * H * d * B * S * (S + 1) / 2        # QK^T and PV, lower triangle incl. diagonal
+    return spec.n_layers * (B * S * per_tok + attn) + 2 * B * spec.vocab_size * D
+
+
+def decode_bytes(spec, B: int, ctx_first: int, steps: int) -> float:
+    """Algorithmic HBM bytes of `steps` decode steps: every weight once per step, the KV
+    cache read over the context, the new K/V written, the logits written."""
+    D, H, G, d, F, V = (spec.dim, spec.n_heads, spec.n_kv_heads, spec.head_dim,
+                        spec.ffn_hidden, spec.vocab_size)
+    w_layer = 2 * (D * (H + 2 * G) * d + H * d * D + 3 * D * F + 2 * D)
+    weights = spec.n_layers * w_layer + 2 * V * D + 2 * D
+    total = 0.0
+    for k in range(steps):
+        ctx = ctx_first + k
+        kv_read = spec.n_layers * B * G * ctx * d * 2 * 2
+        kv_write = spec.n_layers * B * G * d * 2 * 2
+        total += weights + kv_read + kv_write + B * V * 4
+    return total
+
+
+def cpu_baseline(spec, seed: int, S: int, n_layers_sample: int):
+    """Time the CPU oracle (float32) on `n_layers_sample` of the 32 layers of the prefill
+    at S tokens plus the head; scale the per-layer time to the whole stack."""
+    from oracle import llama_oracle as O
+    from llama_decoder_forward_amd import synthetic as syn
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    synth = syn.SyntheticWeights(spec, seed, cache=False)
+    names = ["tok_embeddings.weight", "norm.weight", "output.weight"]
+    for l in range(n_layers_sample):
+        names += [n for n, *_ in syn.layer_weight_specs(spec, l)]
+    W = {n: synth.as_float(n, np.float32) for n in names}
+    toks = syn.tokens(seed, 1, S, spec.vocab_size)[0]
+    t0 = time.perf_counter()
+    x = O.embed(toks, W, np.float32)
+    cache = O.SequenceCache(spec, S, np.float32)
+    t1 = time.perf_counter()
+    for l in range(n_layers_sample):
+        x = O.layer_forward(x, W, spec, l, cache, 0)
+    t2 = time.perf_counter()
+    logits = O.head_logits(x[-1:], W, spec)
+    t3 = time.perf_counter()
+    assert np.isfinite(logits).all()
+    per_layer = (t2 - t1) / n_layers_sample
+    est = (t1 - t0) + per_layer * spec.n_layers + (t3 - t2)
+    return {"value": S / est, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"prefill of 1 x {S} tokens through {n_layers_sample} of "
+                       f"{spec.n_layers} layers plus the head in float32 "
+                       f"({t3 - t0:.1f} s measured); per-layer time scaled to "
+                       f"{spec.n_layers} layers"),
+            "seconds_measured": t3 - t0}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5, help="timed prefill steps")
+    ap.add_argument("--warmup", type=int, default=2, help="untimed prefill steps")
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--decode-batch", type=int, default=32)
+    ap.add_argument("--decode-ctx", type=int, default=4096)
+    ap.add_argument("--seq", type=int, default=2048)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=2)
+    ap.add_argument("--profile-only", action="store_true",
+                    help="a short run for rocprofv3: 1 warmup + --steps prefill, 8 decode steps")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1)", file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+    from llama_decoder_forward_amd import binding as bd
+    from llama_decoder_forward_amd import synthetic as syn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    spec = syn.LLAMA3_8B
+    seed = 3
+    dec_B, dec_ctx, dec_steps = args.decode_batch, args.decode_ctx, args.decode_steps
+    if args.profile_only:
+        dec_steps = min(dec_steps, 8)
+    run_decode = not args.no_decode
+    max_batch = dec_B if run_decode else 1
+    max_seq = max(args.seq, dec_ctx + dec_steps if run_decode else 0)
+    max_tokens = max(args.seq, dec_B * dec_ctx if run_decode else 0)
+
+    t = time.perf_counter()
+    synth = syn.SyntheticWeights(spec, seed, cache=False)
+    weights = bd.upload_weights(synth)
+    torch.cuda.synchronize()
+    log(f"weights generated and uploaded in {time.perf_counter() - t:.1f} s")
+    m = bd.Model(spec, weights, max_batch=max_batch, max_seq=max_seq, max_tokens=max_tokens)
+
+    # ---------------------------------------------------------------- prefill (headline)
+    S = args.seq
+    toks = torch.from_numpy(syn.tokens(seed, 1, S, spec.vocab_size)).cuda()
+    stream = torch.cuda.current_stream()
+    warm = 1 if args.profile_only else args.warmup
+    for _ in range(warm):
+        m.prefill(toks)
+    torch.cuda.synchronize()
+    log("prefill warmup done")
+    m.profile_kernel("ffn_up")
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        m.prefill(toks)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / args.steps
+    k_ms, k_n = m.profile_read()
+    m.profile_kernel("none")
+    m.sync_status()
+    log(f"prefill: {ms_step:.2f} ms/step")
+    flops = prefill_flops(spec, 1, S)
+    ffn_up_flops = 2 * S * 2 * spec.ffn_hidden * spec.dim
+    k_avg = k_ms / max(k_n, 1)
+    ach = ffn_up_flops / (k_avg * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": S / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": warm,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3-8b-shaped causal prefill: 32 layers + lm_head of the last "
+                               "token, batch 1 x 2048 tokens",
+                   "batch": 1, "seq_len": S, "parallelism": "none (1 GPU)"},
+        "prefill_mfma_frac": flops / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "prefill_tflops": flops / (ms_step * 1e-3) / 1e12,
+        "roofline": {"kernel": "ffn_up (W1/W3 GEMM + SiLU*up), M=2048 N=2x14336 K=4096",
+                     "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                     "avg_launch_ms": k_avg, "launches": k_n},
+    }
+
+    # ---------------------------------------------------------------- decode
+    if run_decode:
+        dtoks = torch.from_numpy(syn.tokens(4, dec_B, dec_ctx, spec.vocab_size)).cuda()
+        t = time.perf_counter()
+        lg = m.prefill(dtoks)
+        first = lg.argmax(-1).to(torch.int32).contiguous()
+        torch.cuda.synchronize()
+        log(f"decode setup prefill ({dec_B} x {dec_ctx}) in {time.perf_counter() - t:.1f} s")
+        m.generate(first, dec_ctx, dec_steps)            # warmup (same positions)
+        torch.cuda.synchronize()
+        start.record(stream)
+        out, _ = m.generate(first, dec_ctx, dec_steps)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        dms = start.elapsed_time(stop)
+        m.sync_status()
+        dbytes = decode_bytes(spec, dec_B, dec_ctx + 1, dec_steps)
+        # decode attention kernel timed on eager steps (outside the captured graph)
+        m.profile_kernel("attention")
+        cur = first
+        n_eager = 4
+        for k in range(n_eager):
+            cur, _ = m.decode_step(cur, dec_ctx + k, want_logits=False)
+        torch.cuda.synchronize()
+        a_ms, a_n = m.profile_read()
+        m.profile_kernel("none")
+        a_avg = a_ms / max(a_n, 1)
+        ctx_mid = dec_ctx + 1 + (n_eager - 1) / 2
+        a_bytes = dec_B * spec.n_kv_heads * ctx_mid * spec.head_dim * 2 * 2
+        a_gbs = a_bytes / (a_avg * 1e-3) / 1e9
+        log(f"decode: {dms / dec_steps:.3f} ms/step")
+        result["decode"] = {
+            "value": dec_B * dec_steps / (dms * 1e-3), "unit": "tokens/s",
+            "ms_per_step": dms / dec_steps, "steps": dec_steps, "batch": dec_B,
+            "context": [dec_ctx + 1, dec_ctx + dec_steps],
+            "workload": f"llama3-8b-shaped greedy KV-cache decode, batch {dec_B}, "
+                        f"{dec_ctx} prefilled positions, {dec_steps} steps (HIP graph)",
+            "hbm_gbs": dbytes / (dms * 1e-3) / 1e9,
+            "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "roofline": {"kernel": "decode attention (split-K over the cache)", "bound": "hbm",
+                         "achieved": a_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": a_gbs / PEAK_HBM_GBS, "traffic": None,
+                         "avg_launch_ms": a_avg, "launches": a_n},
+            "tokens_head": out[:4, 0].tolist(),
+        }
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline and not args.profile_only:
+        log("timing the CPU oracle sample")
+        del m, weights
+        torch.cuda.empty_cache()
+        result["cpu_baseline"] = cpu_baseline(spec, seed, S, args.cpu_layers)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

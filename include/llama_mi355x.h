@@ -154,6 +154,27 @@ llama_status llama_layer_forward(llama_model *m, int32_t layer, const float *x_i
  * argmax give INVALID_ARG) and clear them. */
 llama_status llama_sync_status(llama_model *m, hipStream_t stream);
 
+/* Kernel classes of the forward pass, for llama_profile_kernel. */
+typedef enum {
+    LLAMA_KERNEL_NONE = 0,
+    LLAMA_KERNEL_QKV = 1,        /* Q/K/V projection with RoPE and cache write        */
+    LLAMA_KERNEL_ATTENTION = 2,  /* causal GQA attention (prefill or decode)           */
+    LLAMA_KERNEL_WO = 3,         /* output projection with residual add               */
+    LLAMA_KERNEL_FFN_UP = 4,     /* W1/W3 projection with SiLU * up                   */
+    LLAMA_KERNEL_FFN_DOWN = 5,   /* W2 projection with residual add                   */
+    LLAMA_KERNEL_LM_HEAD = 6,    /* vocabulary projection                              */
+    LLAMA_KERNEL_RMSNORM = 7     /* RMSNorm                                            */
+} llama_kernel;
+
+/* Start timing every launch of one kernel class with HIP events recorded on the call's
+ * stream around it (LLAMA_KERNEL_NONE stops).  Launches inside llama_generate's captured
+ * graph are not timed.  Errors: INVALID_ARG. */
+llama_status llama_profile_kernel(llama_model *m, llama_kernel kind);
+
+/* Synchronise on the recorded events and report the summed duration in milliseconds and
+ * the number of timed launches since llama_profile_kernel, then reset the counts. */
+llama_status llama_profile_read(llama_model *m, double *total_ms, int32_t *launches);
+
 /* Release the handle (the caller's buffers are untouched).  NULL is a no-op. */
 void llama_free(llama_model *m);
 

@@ -49,7 +49,10 @@ class LlamaWeights(ctypes.Structure):
 
 EXPORTS = ["llama_kv_cache_bytes", "llama_workspace_bytes", "llama_init_weights", "llama_prefill",
            "llama_decode_step", "llama_generate", "llama_layer_forward", "llama_sync_status",
-           "llama_free", "llama_last_error"]
+           "llama_free", "llama_last_error", "llama_profile_kernel", "llama_profile_read"]
+
+KERNELS = {"none": 0, "qkv": 1, "attention": 2, "wo": 3, "ffn_up": 4, "ffn_down": 5,
+           "lm_head": 6, "rmsnorm": 7}
 
 _lib = None
 
@@ -74,12 +77,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.llama_generate.argtypes = [P, P, I, I, I, P, P, P]
     lib.llama_layer_forward.argtypes = [P, I, P, P, I, I, I, P]
     lib.llama_sync_status.argtypes = [P, P]
+    lib.llama_profile_kernel.argtypes = [P, ctypes.c_int]
+    lib.llama_profile_read.argtypes = [P, F(ctypes.c_double), F(ctypes.c_int32)]
     lib.llama_free.argtypes = [P]
     lib.llama_free.restype = None
     lib.llama_last_error.argtypes = []
     lib.llama_last_error.restype = ctypes.c_char_p
     for fn in ("llama_init_weights", "llama_prefill", "llama_decode_step", "llama_generate",
-               "llama_layer_forward", "llama_sync_status"):
+               "llama_layer_forward", "llama_sync_status", "llama_profile_kernel",
+               "llama_profile_read"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -199,6 +205,16 @@ class Model:
         check(self.lib.llama_layer_forward(self.handle, layer, _ptr(x_in), _ptr(x_out), B, S,
                                            start_pos, _stream(stream)))
         return x_out
+
+    def profile_kernel(self, kind: str):
+        """Time every launch of one kernel class with HIP events (kind in KERNELS)."""
+        check(self.lib.llama_profile_kernel(self.handle, KERNELS[kind]))
+
+    def profile_read(self):
+        """(total milliseconds, launches) timed since profile_kernel; resets the counts."""
+        ms, n = ctypes.c_double(), ctypes.c_int32()
+        check(self.lib.llama_profile_read(self.handle, ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
 
     def sync_status(self, stream=None):
         check(self.lib.llama_sync_status(self.handle, _stream(stream)))

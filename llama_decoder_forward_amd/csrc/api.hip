@@ -110,6 +110,10 @@ struct llama_model {
     hipGraphExec_t graph_exec = nullptr;
     int graph_B = -1, graph_max_ctx = -1;
     int32_t* graph_out = nullptr;
+    // kernel timing (llama_profile_kernel)
+    int prof_kind = LLAMA_KERNEL_NONE;
+    std::vector<hipEvent_t> prof_events;  // pairs: start, stop
+    size_t prof_used = 0;
 
     uint32_t* deverr() { return reinterpret_cast<uint32_t*>(ws + L.flags); }
     int* pos_ctr() { return reinterpret_cast<int*>(ws + L.flags + 64); }
@@ -146,6 +150,32 @@ llama_status ensure_rope(llama_model* m, hipStream_t s) {
     return LLAMA_OK;
 }
 
+// Event pair around launches of the profiled kernel class (skipped during graph capture).
+struct ProfScope {
+    llama_model* m;
+    hipStream_t s;
+    hipEvent_t stop = nullptr;
+    ProfScope(llama_model* m_, int kind, hipStream_t s_) : m(m_), s(s_) {
+        if (m->prof_kind != kind || kind == LLAMA_KERNEL_NONE) return;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+        if (m->prof_used + 2 > m->prof_events.size()) {
+            for (int i = 0; i < 2; ++i) {
+                hipEvent_t e;
+                if (hipEventCreate(&e) != hipSuccess) return;
+                m->prof_events.push_back(e);
+            }
+        }
+        hipEvent_t start = m->prof_events[m->prof_used];
+        stop = m->prof_events[m->prof_used + 1];
+        if (hipEventRecord(start, s) != hipSuccess) { stop = nullptr; return; }
+        m->prof_used += 2;
+    }
+    ~ProfScope() {
+        if (stop) (void)hipEventRecord(stop, s);
+    }
+};
+
 lk::GemmArgs<void> gemm_args(const void* A, int lda, const void* w, int M, int N, int K) {
     lk::GemmArgs<void> g{};
     g.A = A; g.lda = lda;
@@ -164,27 +194,47 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
     const int T = B * S, D = c.dim, H = c.n_heads, G = c.n_kv_heads, d = c.head_dim;
     const int Nq = H * d, Nk = G * d;
 
-    HIP_TRY(lk::rmsnorm(m->dt, xin, 1, 0, w.attention_norm, m->h(), T, D, c.norm_eps, s));
+    {
+        ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
+        HIP_TRY(lk::rmsnorm(m->dt, xin, 1, 0, w.attention_norm, m->h(), T, D, c.norm_eps, s));
+    }
 
     lk::GemmArgs<void> qkv = gemm_args(m->h(), D, w.wq, T, Nq + 2 * Nk, D);
     qkv.W = WeightRows<void>{w.wq, w.wk, w.wv, Nq, Nq + Nk, D};
     EpiQKV<void> eq{m->q(), m->kc(l), m->vc(l), m->rope(), Nq, Nk, d, S, start_pos, G,
                     m->seq_stride, pos_dev};
-    HIP_TRY(lk::gemm_qkv(m->dt, qkv, eq, s));
+    {
+        ProfScope ps(m, LLAMA_KERNEL_QKV, s);
+        HIP_TRY(lk::gemm_qkv(m->dt, qkv, eq, s));
+    }
 
     lk::AttnArgs aa{m->q(), m->kc(l), m->vc(l), m->attn(), B, S, start_pos, H, G, d,
                     m->seq_stride, pos_dev, m->partials(), max_ctx};
-    if (decode) HIP_TRY(lk::attention_decode(m->dt, aa, s));
-    else HIP_TRY(lk::attention_prefill(m->dt, aa, s));
-
-    HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m->attn(), Nq, w.wo, T, D, Nq),
-                              EpiResidual{xin, xout, D}, s));
-    HIP_TRY(lk::rmsnorm(m->dt, xout, 1, 0, w.ffn_norm, m->h(), T, D, c.norm_eps, s));
+    {
+        ProfScope ps(m, LLAMA_KERNEL_ATTENTION, s);
+        if (decode) HIP_TRY(lk::attention_decode(m->dt, aa, s));
+        else HIP_TRY(lk::attention_prefill(m->dt, aa, s));
+    }
+    {
+        ProfScope ps(m, LLAMA_KERNEL_WO, s);
+        HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m->attn(), Nq, w.wo, T, D, Nq),
+                                  EpiResidual{xin, xout, D}, s));
+    }
+    {
+        ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
+        HIP_TRY(lk::rmsnorm(m->dt, xout, 1, 0, w.ffn_norm, m->h(), T, D, c.norm_eps, s));
+    }
     lk::GemmArgs<void> ff = gemm_args(m->h(), D, w.w1, T, c.ffn_hidden, D);
     ff.W3 = WeightRows<void>{w.w3, w.w3, w.w3, c.ffn_hidden, c.ffn_hidden, D};
-    HIP_TRY(lk::gemm_swiglu(m->dt, ff, m->g(), c.ffn_hidden, s));
-    HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m->g(), c.ffn_hidden, w.w2, T, D, c.ffn_hidden),
-                              EpiResidual{xout, xout, D}, s));
+    {
+        ProfScope ps(m, LLAMA_KERNEL_FFN_UP, s);
+        HIP_TRY(lk::gemm_swiglu(m->dt, ff, m->g(), c.ffn_hidden, s));
+    }
+    {
+        ProfScope ps(m, LLAMA_KERNEL_FFN_DOWN, s);
+        HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m->g(), c.ffn_hidden, w.w2, T, D, c.ffn_hidden),
+                                  EpiResidual{xout, xout, D}, s));
+    }
     return LLAMA_OK;
 }
 
@@ -192,9 +242,15 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
 // starting at `offset` (article, section 预测下一个输出).
 llama_status run_head(llama_model* m, int rows, int step, int offset, float* logits, hipStream_t s) {
     const llama_config& c = m->cfg;
-    HIP_TRY(lk::rmsnorm(m->dt, m->x(), step, offset, m->norm, m->h(), rows, c.dim, c.norm_eps, s));
-    HIP_TRY(lk::gemm_store_f32(m->dt, gemm_args(m->h(), c.dim, m->output, rows, c.vocab_size, c.dim),
-                               EpiStoreF32{logits, c.vocab_size}, s));
+    {
+        ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
+        HIP_TRY(lk::rmsnorm(m->dt, m->x(), step, offset, m->norm, m->h(), rows, c.dim, c.norm_eps, s));
+    }
+    {
+        ProfScope ps(m, LLAMA_KERNEL_LM_HEAD, s);
+        HIP_TRY(lk::gemm_store_f32(m->dt, gemm_args(m->h(), c.dim, m->output, rows, c.vocab_size, c.dim),
+                                   EpiStoreF32{logits, c.vocab_size}, s));
+    }
     return LLAMA_OK;
 }
 
@@ -387,8 +443,33 @@ llama_status llama_sync_status(llama_model* m, hipStream_t s) {
     return LLAMA_OK;
 }
 
+llama_status llama_profile_kernel(llama_model* m, llama_kernel kind) {
+    if (!m) return fail(LLAMA_ERR_INVALID_ARG, "NULL model");
+    if ((int)kind < LLAMA_KERNEL_NONE || (int)kind > LLAMA_KERNEL_RMSNORM)
+        return fail(LLAMA_ERR_INVALID_ARG, "unknown kernel class %d", (int)kind);
+    m->prof_kind = kind;
+    m->prof_used = 0;
+    return LLAMA_OK;
+}
+
+llama_status llama_profile_read(llama_model* m, double* total_ms, int32_t* launches) {
+    if (!m || !total_ms || !launches) return fail(LLAMA_ERR_INVALID_ARG, "NULL argument");
+    double total = 0.0;
+    for (size_t i = 0; i + 1 < m->prof_used; i += 2) {
+        HIP_TRY(hipEventSynchronize(m->prof_events[i + 1]));
+        float ms = 0.0f;
+        HIP_TRY(hipEventElapsedTime(&ms, m->prof_events[i], m->prof_events[i + 1]));
+        total += ms;
+    }
+    *total_ms = total;
+    *launches = (int32_t)(m->prof_used / 2);
+    m->prof_used = 0;
+    return LLAMA_OK;
+}
+
 void llama_free(llama_model* m) {
     if (!m) return;
+    for (hipEvent_t e : m->prof_events) (void)hipEventDestroy(e);
     if (m->graph_exec) (void)hipGraphExecDestroy(m->graph_exec);
     if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
     delete m;
