@@ -83,14 +83,412 @@ hipError_t launch_generic(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------
+// Prefill, bf16, head_dim 128: flash-style attention on the matrix cores.
+//
+// One workgroup (4 waves) takes one (sequence b, KV head g) and a block of BQ = 128/group
+// positions for all `group` = H/G query heads that read KV head g, i.e. 128 query rows
+// sharing every K/V tile it stages.  Wave w owns query rows 32w..32w+31 (row r: head
+// g*group + r / BQ, position r % BQ).  Keys go through LDS in blocks of 64 (double
+// buffered); each block does
+//   S^T = K Q^T      (MFMA A = K rows, B = the wave's Q held in registers)
+//   online softmax   (each lane owns one query column: max/sum over its 32 values and the
+//                     partner lane l^32; rescaling O needs no data exchange)
+//   O^T += V^T P^T   (A = V^T from the transposed cache, B = P^T straight from registers,
+//                     P rounded to bf16 as the article casts the softmax output)
+// Keys beyond the block's last position are never read; keys after a row's own position
+// get a score of -inf (article, section 多头注意力: the upper-triangular -inf mask).
+// ------------------------------------------------------------------------------------
+constexpr int FA_D = 128, FA_BKV = 64, FA_ROWS = 128;
+constexpr int FA_KCH = FA_BKV * FA_D / 8;       // 16-byte chunks of a K tile (1024)
+constexpr int FA_VCH = FA_D * FA_BKV / 4;       // 8-byte chunks of a V^T tile (2048)
+constexpr size_t FA_STAGE_BYTES = FA_KCH * 16 + FA_VCH * 8;  // 32 KB
+
+__device__ __forceinline__ u32x4 mask_keys8(u32x4 v, int first_key, int limit) {
+    // zero the bf16 elements whose key index (first_key + e) is >= limit
+    if (first_key + 8 <= limit) return v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int k0 = first_key + 2 * w;
+        uint32_t x = v[w];
+        if (k0 >= limit) x &= 0xFFFF0000u;
+        if (k0 + 1 >= limit) x &= 0x0000FFFFu;
+        v[w] = x;
+    }
+    return v;
+}
+
+__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
+    bf16* __restrict__ out, int S, int start_pos, int H, int G, int seq_stride,
+    float scale_log2, int nqb) {
+    extern __shared__ u32x4 fa_smem[];
+    const int group = H / G, BQ = FA_ROWS / group;
+    const int GB = gridDim.x / nqb;
+    const int qb = nqb - 1 - (int)blockIdx.x / GB;  // heaviest (latest) query blocks first
+    const int gb = (int)blockIdx.x % GB;
+    const int b = gb / G, g = gb % G;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, lr = lane & 31, lh = lane >> 5;
+
+    // this lane's query row
+    const int r = wave * 32 + lr;
+    const int hq = g * group + r / BQ;
+    const int sq = qb * BQ + r % BQ;
+    const bool qvalid = sq < S;
+    const int qpos = start_pos + sq;
+    const int p_lo = start_pos + qb * BQ;
+    const int p_hi = start_pos + min(S, qb * BQ + BQ) - 1;
+    const int ctx = p_hi + 1;                 // keys this block needs: 0..p_hi
+    const int nkb = (ctx + FA_BKV - 1) / FA_BKV;
+
+    bf16x8 qf[8];
+    {
+        const bf16* qrow = q + ((size_t)(b * S + (qvalid ? sq : 0)) * H + hq) * FA_D;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + (kk * 2 + lh) * 8)
+                            : bf16x8{};
+    }
+
+    const bf16* kbase = kc + ((size_t)b * G + g) * seq_stride * FA_D;
+    const bf16* vbase = vc + ((size_t)b * G + g) * FA_D * seq_stride;
+
+    // loaders: K chunk idx = t + 256 i -> key row idx/16, 16-byte chunk idx%16;
+    //          V^T chunk idx = t + 256 i -> d row idx/8, keys 8*(idx%8)..+7
+    u32x4 kreg[4], vreg[4];
+    auto gload = [&](int kb) {
+        const int kv0 = kb * FA_BKV;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = t + 256 * i;
+            const int kr = idx >> 4, kcn = idx & 15;
+            kreg[i] = (kv0 + kr < ctx)
+                          ? *reinterpret_cast<const u32x4*>(kbase + (size_t)(kv0 + kr) * FA_D + kcn * 8)
+                          : u32x4{0, 0, 0, 0};
+            const int vd = idx >> 3, vcn = idx & 7;
+            const int key = kv0 + vcn * 8;
+            u32x4 v = (key < ctx) ? *reinterpret_cast<const u32x4*>(vbase + (size_t)vd * seq_stride + key)
+                                  : u32x4{0, 0, 0, 0};
+            vreg[i] = mask_keys8(v, key, ctx);
+        }
+    };
+    auto swrite = [&](int st) {
+        u32x4* ks = fa_smem + st * (FA_STAGE_BYTES / 16);
+        uint2* vs = reinterpret_cast<uint2*>(ks + FA_KCH);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = t + 256 * i;
+            const int kr = idx >> 4, kcn = idx & 15;
+            ks[kr * 16 + (kcn ^ (kr & 7))] = kreg[i];
+            const int vd = idx >> 3, vcn = idx & 7;
+            vs[vd * 16 + ((2 * vcn) ^ (vd & 15))] = make_uint2(vreg[i][0], vreg[i][1]);
+            vs[vd * 16 + ((2 * vcn + 1) ^ (vd & 15))] = make_uint2(vreg[i][2], vreg[i][3]);
+        }
+    };
+
+    f32x16 oacc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    gload(0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int st = kb & 1;
+        swrite(st);
+        __syncthreads();
+        if (kb + 1 < nkb) gload(kb + 1);
+        const u32x4* ks = fa_smem + st * (FA_STAGE_BYTES / 16);
+        const uint2* vs = reinterpret_cast<const uint2*>(ks + FA_KCH);
+        const int kv0 = kb * FA_BKV;
+
+        // S^T = K Q^T: two 32-key tiles
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int ch = (kk * 2 + lh) ^ (lr & 7);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, ks[(32 * i + lr) * 16 + ch]);
+                sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[i], 0, 0, 0);
+            }
+        }
+        // scale, mask, block max; register 4g+q of tile i is key kv0 + 32i + 8g + 4lh + q
+        const bool need_mask = kv0 + FA_BKV - 1 > p_lo;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float sv = sacc[i][e] * scale_log2;
+                if (need_mask) {
+                    const int key = kv0 + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+                    if (key > qpos) sv = -INFINITY;
+                }
+                sacc[i][e] = sv;
+                mx = fmaxf(mx, sv);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = exp2f(m_run - m_new);
+        float psum = 0.0f;
+        bf16x8 pf[4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = exp2f(sacc[i][e] - m_new);
+                psum += p;
+                sacc[i][e] = p;
+            }
+        // P^T operand of k-step j (keys 32(j/2) + 16(j%2) + [0,16)): slot s of lane lh is
+        // key 32(j/2) + 16(j%2) + 8(s/4) + 4lh + s%4, i.e. registers 4(2(j%2) + s/4) + s%4
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                pf[j][s] = from_f32<bf16>(sacc[j >> 1][4 * (2 * (j & 1) + (s >> 2)) + (s & 3)]);
+        psum += __shfl_xor(psum, 32, 64);
+        l_run = l_run * corr + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int td = 0; td < 4; ++td)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[td][e] *= corr;
+
+        // O^T += V^T P^T: V^T slot s of lane lh is key kbase_j + 8(s/4) + 4lh + s%4, i.e.
+        // the 8-byte chunks (kbase_j/4 + lh) and (kbase_j/4 + 2 + lh) of row d
+#pragma unroll
+        for (int td = 0; td < 4; ++td) {
+            const int d = 32 * td + lr;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c1 = (8 * (j >> 1) + 4 * (j & 1)) + lh;
+                const uint2 lo = vs[d * 16 + (c1 ^ (d & 15))];
+                const uint2 hi = vs[d * 16 + ((c1 + 2) ^ (d & 15))];
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+                oacc[td] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], oacc[td], 0, 0, 0);
+            }
+        }
+    }
+
+    if (!qvalid) return;
+    const float inv = 1.0f / l_run;
+    bf16* orow = out + ((size_t)(b * S + sq) * H + hq) * FA_D;
+#pragma unroll
+    for (int td = 0; td < 4; ++td)
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            float v[4] = {oacc[td][4 * gg] * inv, oacc[td][4 * gg + 1] * inv,
+                          oacc[td][4 * gg + 2] * inv, oacc[td][4 * gg + 3] * inv};
+            store4(orow + 32 * td + 8 * gg + 4 * lh, v);
+        }
+}
+
+hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
+    const int group = a.H / a.G, BQ = FA_ROWS / group;
+    const int nqb = (a.S + BQ - 1) / BQ;
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_D);
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_mfma_kernel,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(2 * FA_STAGE_BYTES));
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    attn_prefill_mfma_kernel<<<nqb * a.G * a.B, 256, 2 * FA_STAGE_BYTES, s>>>(
+        (const bf16*)a.q, (const bf16*)a.kc, (const bf16*)a.vc, (bf16*)a.out, a.S, a.start_pos,
+        a.H, a.G, a.seq_stride, scale_log2, nqb);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------
+// Decode, bf16, head_dim 128: split-K over the cached context on the matrix cores.
+//
+// Workgroup = (split of DEC_CHUNK keys, KV head g, sequence b), 4 waves of 64 keys each.
+// A wave streams its 64 keys of K (16 KB) and V^T (16 KB) straight from HBM into MFMA
+// operand registers (16x16x32 bf16; the `group` query heads of g are the B-operand
+// columns, the rest zero), computes S^T = K Q^T, a local softmax, O^T = V^T P^T, and
+// writes one partial (max, sum, unnormalised o[128]) per query head.  A second kernel
+// merges the partials of every wave that holds at least one key.  Contiguous 64-byte
+// runs per lane: lane quarter kq takes d = 32kq..32kq+31 of each key row (the k index of
+// the MFMA is permuted identically on both operands).
+// ------------------------------------------------------------------------------------
+constexpr int DEC_KEYS_PER_WAVE = 64;
+constexpr int DEC_CHUNK = 4 * DEC_KEYS_PER_WAVE;  // keys per workgroup (256)
+
+__global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
+    float* __restrict__ part, int start_pos, const int* pos_dev, int H, int G, int seq_stride,
+    int max_parts, float scale_log2) {
+    const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int pos = pos_dev ? *pos_dev : start_pos;
+    const int ctx = pos + 1;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int k0 = split * DEC_CHUNK + wave * DEC_KEYS_PER_WAVE;
+    if (k0 >= ctx) return;  // nothing cached here; the merge skips this partial
+    const int group = H / G;
+    const int col = lane & 15, kq = lane >> 4;
+
+    // B operand Q^T: lane (col, kq) supplies d = 32kq + 8j .. +7 for k-step j
+    bf16x8 qf[4];
+    {
+        const bool real = col < group;
+        const bf16* qrow = q + ((size_t)b * H + g * group + (real ? col : 0)) * FA_D + 32 * kq;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            qf[j] = real ? *reinterpret_cast<const bf16x8*>(qrow + 8 * j) : bf16x8{};
+    }
+    const bf16* kbase = kc + ((size_t)b * G + g) * seq_stride * FA_D;
+    const bf16* vbase = vc + ((size_t)b * G + g) * FA_D * seq_stride;
+
+    // K: 4 tiles of 16 keys; lane row = key k0 + 16t + col, 64 bytes at d = 32kq
+    u32x4 kr[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int key = k0 + 16 * tt + col;
+        const bf16* src = kbase + (size_t)key * FA_D + 32 * kq;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            kr[tt][j] = (key < ctx) ? *reinterpret_cast<const u32x4*>(src + 8 * j) : u32x4{0, 0, 0, 0};
+    }
+    // V^T: 8 tiles of 16 d-rows x 2 k-steps of 32 keys; slot s of lane kq is key
+    // k0 + 32j + 16(s/4) + 4kq + s%4: two 8-byte loads per (tile, step)
+    uint2 vr[8][2][2];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        const bf16* row = vbase + (size_t)(16 * dt + col) * seq_stride;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const int key = k0 + 32 * j + 16 * h2 + 4 * kq;
+                uint2 v = (key < ctx) ? *reinterpret_cast<const uint2*>(row + key) : make_uint2(0, 0);
+                if (key + 4 > ctx) {  // partial: zero keys >= ctx
+                    if (key + 0 >= ctx) v.x &= 0xFFFF0000u;
+                    if (key + 1 >= ctx) v.x &= 0x0000FFFFu;
+                    if (key + 2 >= ctx) v.y &= 0xFFFF0000u;
+                    if (key + 3 >= ctx) v.y &= 0x0000FFFFu;
+                }
+                vr[dt][j][h2] = v;
+            }
+    }
+
+    // S^T tiles: lane (col, kq) register e of tile t is key k0 + 16t + 4kq + e
+    f32x4 sacc[4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        sacc[tt] = f32x4{};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, kr[tt][j]), qf[j], sacc[tt], 0, 0, 0);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int key = k0 + 16 * tt + 4 * kq + e;
+            float sv = sacc[tt][e] * scale_log2;
+            if (key >= ctx) sv = -INFINITY;
+            sacc[tt][e] = sv;
+            mx = fmaxf(mx, sv);
+        }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float psum = 0.0f;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float p = exp2f(sacc[tt][e] - mx);
+            psum += p;
+            pf[tt >> 1][4 * (tt & 1) + e] = from_f32<bf16>(p);
+        }
+    psum += __shfl_xor(psum, 16, 64);
+    psum += __shfl_xor(psum, 32, 64);
+
+    // O^T = V^T P^T: 8 d-tiles; lane (col, kq) register e of tile dt is d = 16dt + 4kq + e
+    f32x4 oacc[8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        oacc[dt] = f32x4{};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const bf16x8 a = __builtin_bit_cast(
+                bf16x8, u32x4{vr[dt][j][0].x, vr[dt][j][0].y, vr[dt][j][1].x, vr[dt][j][1].y});
+            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[j], oacc[dt], 0, 0, 0);
+        }
+    }
+    if (col >= group) return;
+    const int h = g * group + col;
+    const int pidx = split * 4 + wave;
+    float* pp = part + ((size_t)(b * H + h) * max_parts + pidx) * (FA_D + 2);
+    if (kq == 0) { pp[0] = mx; pp[1] = psum; }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4*>(pp + 2 + 16 * dt + 4 * kq) = oacc[dt];
+}
+
+// Merge the partials of one (sequence, head): o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+template <typename T>
+__global__ __launch_bounds__(128) void attn_decode_merge_kernel(const float* __restrict__ part,
+                                                                T* __restrict__ out, int start_pos,
+                                                                const int* pos_dev, int H,
+                                                                int d, int max_parts,
+                                                                int keys_per_part) {
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int pos = pos_dev ? *pos_dev : start_pos;
+    const int nparts = (pos + 1 + keys_per_part - 1) / keys_per_part;
+    const float* pp = part + (size_t)(b * H + h) * max_parts * (d + 2);
+    float M = -INFINITY;
+    for (int p = 0; p < nparts; ++p) M = fmaxf(M, pp[(size_t)p * (d + 2)]);
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+        float num = 0.0f, den = 0.0f;
+        for (int p = 0; p < nparts; ++p) {
+            const float* q = pp + (size_t)p * (d + 2);
+            const float w = exp2f(q[0] - M);
+            den += w * q[1];
+            num += w * q[2 + i];
+        }
+        out[(size_t)b * H * d + (size_t)h * d + i] = from_f32<T>(num / den);
+    }
+}
+
+hipError_t launch_decode_mfma(const AttnArgs& a, hipStream_t s) {
+    const int splits = (a.max_ctx + DEC_CHUNK - 1) / DEC_CHUNK;
+    const int max_parts = a.seq_stride / DEC_KEYS_PER_WAVE;
+    const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_D);
+    attn_decode_mfma_kernel<<<dim3(splits, a.G, a.B), 256, 0, s>>>(
+        (const bf16*)a.q, (const bf16*)a.kc, (const bf16*)a.vc, a.partials, a.start_pos,
+        a.pos_dev, a.H, a.G, a.seq_stride, max_parts, scale_log2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    attn_decode_merge_kernel<bf16><<<dim3(a.H, a.B), 128, 0, s>>>(
+        a.partials, (bf16*)a.out, a.start_pos, a.pos_dev, a.H, FA_D, max_parts,
+        DEC_KEYS_PER_WAVE);
+    return hipGetLastError();
+}
+
+bool mfma_path(const AttnArgs& a) {
+    const int group = a.H / a.G;
+    return a.d == FA_D && group <= 16 && FA_ROWS % group == 0;
+}
+
 }  // namespace
 
 hipError_t attention_prefill(Dt dt, const AttnArgs& a, hipStream_t s) {
+    if (a.B * a.S == 0) return hipSuccess;
+    if (dt == Dt::BF16 && mfma_path(a)) return launch_prefill_mfma(a, s);
     if (dt == Dt::BF16) return launch_generic<bf16>(a, s);
     return launch_generic<float>(a, s);
 }
 
 hipError_t attention_decode(Dt dt, const AttnArgs& a, hipStream_t s) {
+    if (a.B == 0) return hipSuccess;
+    if (dt == Dt::BF16 && mfma_path(a)) return launch_decode_mfma(a, s);
     if (dt == Dt::BF16) return launch_generic<bf16>(a, s);
     return launch_generic<float>(a, s);
 }

@@ -142,6 +142,48 @@ def test_bf16_teacher_forced_decode():
     m.sync_status()
 
 
+def test_bf16_long_context_decode_multiple_splits():
+    say("small bf16 stack: prefill S=600 (several decode splits, ragged) then 3 decode steps, B=2")
+    spec = small_bf16_spec()
+    B, S, steps = 2, 600, 3
+    m, synth = build_model(spec, 8, max_batch=B, max_seq=640, max_tokens=B * S)
+    toks = syn.tokens(8, B, S, spec.vocab_size)
+    W = syn.FloatView(synth)
+    ref0, caches = O.prefill(toks, W, spec, capacity=S + steps)
+    got0 = m.prefill(torch.from_numpy(toks).cuda()).cpu().numpy()
+    assert_rows_close(got0, ref0, BF16_TOL, "prefill last logits")
+    cur = O.argmax(ref0).astype(np.int32)
+    for k in range(steps):
+        ref = O.decode_step(cur, S + k, W, spec, caches)
+        nxt, lg = m.decode_step(torch.from_numpy(cur).cuda(), S + k)
+        lg = lg.cpu().numpy()
+        assert_rows_close(lg, ref, BF16_TOL, f"decode step {k}")
+        check_argmax(nxt.cpu().numpy(), lg, ref, f"decode step {k}")
+        cur = O.argmax(ref).astype(np.int32)
+
+
+def test_bf16_generate_graph_matches_eager_decode():
+    say("small bf16 stack: generate (captured graph) vs eager decode steps, B=3")
+    spec = small_bf16_spec()
+    B, S, steps = 3, 70, 10
+    m, _ = build_model(spec, 9, max_batch=B, max_seq=96, max_tokens=B * S)
+    toks = torch.from_numpy(syn.tokens(9, B, S, spec.vocab_size)).cuda()
+    first = m.prefill(toks).argmax(-1).to(torch.int32).contiguous()
+    eager = []
+    cur = first
+    for k in range(steps):
+        cur, _ = m.decode_step(cur, S + k, want_logits=False)
+        eager.append(cur.clone())
+    eager = torch.stack(eager)
+    m.prefill(toks)
+    out, _ = m.generate(first, S, steps)
+    assert torch.equal(out, eager)
+    m.prefill(toks)
+    out2, lg = m.generate(first, S, steps, want_logits=True)
+    assert torch.equal(out2, eager)
+    assert torch.equal(lg.argmax(-1).to(torch.int32), eager)
+
+
 def test_bf16_chunked_layer_forward():
     say("small bf16 layer: chunked prefill 40 + 37 + 1 tokens")
     spec = small_bf16_spec(n_layers=1)
