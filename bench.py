@@ -203,7 +203,7 @@ def main() -> int:
         dms = start.elapsed_time(stop)
         m.sync_status()
         dbytes = decode_bytes(spec, dec_B, dec_ctx + 1, dec_steps)
-        # decode attention kernel timed on eager steps (outside the captured graph)
+        # decode attention kernel timed on separate decode steps
         m.profile_kernel("attention")
         cur = first
         n_eager = 4
@@ -222,7 +222,7 @@ def main() -> int:
             "ms_per_step": dms / dec_steps, "steps": dec_steps, "batch": dec_B,
             "context": [dec_ctx + 1, dec_ctx + dec_steps],
             "workload": f"llama3-8b-shaped greedy KV-cache decode, batch {dec_B}, "
-                        f"{dec_ctx} prefilled positions, {dec_steps} steps (HIP graph)",
+                        f"{dec_ctx} prefilled positions, {dec_steps} steps (llama_generate)",
             "hbm_gbs": dbytes / (dms * 1e-3) / 1e9,
             "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "roofline": {"kernel": "decode attention (split-K over the cache)", "bound": "hbm",

@@ -133,10 +133,10 @@ llama_status llama_decode_step(llama_model *m, const int32_t *tokens, int32_t B,
                                float *logits, int32_t *next_tokens, hipStream_t stream);
 
 /* n_steps greedy decode steps starting with tokens[b] at position pos: step k runs at
- * position pos+k on the previous step's argmax, entirely on the device (the step is
- * captured once into a HIP graph and replayed).  Writes out_tokens[k*B + b], the argmax
- * of step k; if logits is not NULL also the logits [n_steps,B,V].  Needs
- * pos + n_steps <= max_seq. */
+ * position pos+k on the previous step's argmax.  The position and step index live in
+ * device memory, so the whole loop is enqueued at once with no host synchronisation.
+ * Writes out_tokens[k*B + b], the argmax of step k; if logits is not NULL also the logits
+ * [n_steps,B,V].  Needs pos + n_steps <= max_seq. */
 llama_status llama_generate(llama_model *m, const int32_t *tokens, int32_t B, int32_t pos,
                             int32_t n_steps, int32_t *out_tokens, float *logits,
                             hipStream_t stream);
@@ -167,8 +167,8 @@ typedef enum {
 } llama_kernel;
 
 /* Start timing every launch of one kernel class with HIP events recorded on the call's
- * stream around it (LLAMA_KERNEL_NONE stops).  Launches inside llama_generate's captured
- * graph are not timed.  Errors: INVALID_ARG. */
+ * stream around it (LLAMA_KERNEL_NONE stops).  Launches recorded into a stream capture are
+ * not timed.  Errors: INVALID_ARG. */
 llama_status llama_profile_kernel(llama_model *m, llama_kernel kind);
 
 /* Synchronise on the recorded events and report the summed duration in milliseconds and

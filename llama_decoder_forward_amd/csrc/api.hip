@@ -34,7 +34,7 @@ size_t elem_size(const llama_config& c) { return c.dtype == LLAMA_BF16 ? 2 : 4; 
 
 // Workspace regions, in order, each 256-byte aligned.
 struct Layout {
-    size_t flags, rope, x, h, q, attn, g, logits, partials, tokbuf, total;
+    size_t flags, rope, x, h, q, attn, g, logits, partials, tokbuf, argmax, total;
 };
 
 constexpr int kDecodeChunk = 64;  // key positions per split of the decode attention
@@ -57,6 +57,7 @@ Layout layout_of(const llama_config& c) {
     L.logits = take((size_t)c.max_batch * c.vocab_size * 4);
     L.partials = take((size_t)c.max_batch * c.n_heads * splits * (c.head_dim + 2) * 4);
     L.tokbuf = take((size_t)c.max_batch * 4);
+    L.argmax = take(lk::argmax_scratch_bytes(c.max_batch, c.vocab_size));
     L.total = off;
     return L;
 }
@@ -105,11 +106,6 @@ struct llama_model {
     size_t es = 2;
     int seq_stride = 0;
     bool rope_ready = false;
-    // decode-loop graph
-    hipStream_t capture_stream = nullptr;
-    hipGraphExec_t graph_exec = nullptr;
-    int graph_B = -1, graph_max_ctx = -1;
-    int32_t* graph_out = nullptr;
     // kernel timing (llama_profile_kernel)
     int prof_kind = LLAMA_KERNEL_NONE;
     std::vector<hipEvent_t> prof_events;  // pairs: start, stop
@@ -127,6 +123,7 @@ struct llama_model {
     float* logits_scratch() { return reinterpret_cast<float*>(ws + L.logits); }
     float* partials() { return reinterpret_cast<float*>(ws + L.partials); }
     int* tokbuf() { return reinterpret_cast<int*>(ws + L.tokbuf); }
+    void* argmax_scratch() { return ws + L.argmax; }
     size_t kv_layer_elems() const {
         return (size_t)cfg.max_batch * cfg.n_kv_heads * seq_stride * cfg.head_dim;
     }
@@ -150,7 +147,7 @@ llama_status ensure_rope(llama_model* m, hipStream_t s) {
     return LLAMA_OK;
 }
 
-// Event pair around launches of the profiled kernel class (skipped during graph capture).
+// Event pair around launches of the profiled kernel class (skipped during stream capture).
 struct ProfScope {
     llama_model* m;
     hipStream_t s;
@@ -176,7 +173,7 @@ struct ProfScope {
     }
 };
 
-lk::GemmArgs<void> gemm_args(const void* A, int lda, const void* w, int M, int N, int K) {
+lk::GemmArgs<void> gemm_args(llama_model*, const void* A, int lda, const void* w, int M, int N, int K) {
     lk::GemmArgs<void> g{};
     g.A = A; g.lda = lda;
     g.W = WeightRows<void>{w, w, w, N, N, K};
@@ -199,7 +196,7 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
         HIP_TRY(lk::rmsnorm(m->dt, xin, 1, 0, w.attention_norm, m->h(), T, D, c.norm_eps, s));
     }
 
-    lk::GemmArgs<void> qkv = gemm_args(m->h(), D, w.wq, T, Nq + 2 * Nk, D);
+    lk::GemmArgs<void> qkv = gemm_args(m, m->h(), D, w.wq, T, Nq + 2 * Nk, D);
     qkv.W = WeightRows<void>{w.wq, w.wk, w.wv, Nq, Nq + Nk, D};
     EpiQKV<void> eq{m->q(), m->kc(l), m->vc(l), m->rope(), Nq, Nk, d, S, start_pos, G,
                     m->seq_stride, pos_dev};
@@ -217,14 +214,14 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
     }
     {
         ProfScope ps(m, LLAMA_KERNEL_WO, s);
-        HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m->attn(), Nq, w.wo, T, D, Nq),
+        HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m, m->attn(), Nq, w.wo, T, D, Nq),
                                   EpiResidual{xin, xout, D}, s));
     }
     {
         ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
         HIP_TRY(lk::rmsnorm(m->dt, xout, 1, 0, w.ffn_norm, m->h(), T, D, c.norm_eps, s));
     }
-    lk::GemmArgs<void> ff = gemm_args(m->h(), D, w.w1, T, c.ffn_hidden, D);
+    lk::GemmArgs<void> ff = gemm_args(m, m->h(), D, w.w1, T, c.ffn_hidden, D);
     ff.W3 = WeightRows<void>{w.w3, w.w3, w.w3, c.ffn_hidden, c.ffn_hidden, D};
     {
         ProfScope ps(m, LLAMA_KERNEL_FFN_UP, s);
@@ -232,7 +229,7 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
     }
     {
         ProfScope ps(m, LLAMA_KERNEL_FFN_DOWN, s);
-        HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m->g(), c.ffn_hidden, w.w2, T, D, c.ffn_hidden),
+        HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m, m->g(), c.ffn_hidden, w.w2, T, D, c.ffn_hidden),
                                   EpiResidual{xout, xout, D}, s));
     }
     return LLAMA_OK;
@@ -248,7 +245,7 @@ llama_status run_head(llama_model* m, int rows, int step, int offset, float* log
     }
     {
         ProfScope ps(m, LLAMA_KERNEL_LM_HEAD, s);
-        HIP_TRY(lk::gemm_store_f32(m->dt, gemm_args(m->h(), c.dim, m->output, rows, c.vocab_size, c.dim),
+        HIP_TRY(lk::gemm_store_f32(m->dt, gemm_args(m, m->h(), c.dim, m->output, rows, c.vocab_size, c.dim),
                                    EpiStoreF32{logits, c.vocab_size}, s));
     }
     return LLAMA_OK;
@@ -267,7 +264,8 @@ llama_status run_decode_step(llama_model* m, const int32_t* tokens, int B, int p
     float* lg = logits ? logits : m->logits_scratch();
     llama_status st = run_head(m, B, 1, 0, lg, s);
     if (st != LLAMA_OK) return st;
-    HIP_TRY(lk::argmax(lg, B, c.vocab_size, next, log_out, B, step_ctr, m->deverr(), s));
+    HIP_TRY(lk::argmax(lg, B, c.vocab_size, next, log_out, B, step_ctr, m->argmax_scratch(),
+                       m->deverr(), s));
     return LLAMA_OK;
 }
 
@@ -372,42 +370,15 @@ llama_status llama_generate(llama_model* m, const int32_t* tokens, int32_t B, in
     const int max_ctx = pos + n_steps;
     HIP_TRY(lk::copy_tokens(tokens, m->tokbuf(), B, s));
     HIP_TRY(lk::set_counters(m->pos_ctr(), pos, m->step_ctr(), s));
-    if (logits) {
-        // logits of every step requested: run the steps eagerly, one logits slice each
-        for (int k = 0; k < n_steps; ++k) {
-            st = run_decode_step(m, m->tokbuf(), B, 0, m->pos_ctr(), max_ctx,
-                                 logits + (size_t)k * B * c.vocab_size, m->tokbuf(), out_tokens,
-                                 m->step_ctr(), s);
-            if (st != LLAMA_OK) return st;
-            HIP_TRY(lk::bump_counters(m->pos_ctr(), m->step_ctr(), s));
-        }
-        return LLAMA_OK;
+    // The step reads its position and step index from device memory, so the same launch
+    // sequence repeats with no host round trip; the argmax of each step feeds the next.
+    for (int k = 0; k < n_steps; ++k) {
+        st = run_decode_step(m, m->tokbuf(), B, 0, m->pos_ctr(), max_ctx,
+                             logits ? logits + (size_t)k * B * c.vocab_size : nullptr,
+                             m->tokbuf(), out_tokens, m->step_ctr(), s);
+        if (st != LLAMA_OK) return st;
+        HIP_TRY(lk::bump_counters(m->pos_ctr(), m->step_ctr(), s));
     }
-    // capture one position-independent step (position and step index live in device memory)
-    if (!m->graph_exec || m->graph_B != B || m->graph_max_ctx < max_ctx || m->graph_out != out_tokens) {
-        if (m->graph_exec) { (void)hipGraphExecDestroy(m->graph_exec); m->graph_exec = nullptr; }
-        if (!m->capture_stream) HIP_TRY(hipStreamCreateWithFlags(&m->capture_stream, hipStreamNonBlocking));
-        const int cap_ctx = std::max(max_ctx, std::min(c.max_seq, max_ctx + 256));
-        HIP_TRY(hipStreamBeginCapture(m->capture_stream, hipStreamCaptureModeThreadLocal));
-        st = run_decode_step(m, m->tokbuf(), B, 0, m->pos_ctr(), cap_ctx, nullptr, m->tokbuf(),
-                             out_tokens, m->step_ctr(), m->capture_stream);
-        hipError_t be = lk::bump_counters(m->pos_ctr(), m->step_ctr(), m->capture_stream);
-        hipGraph_t graph = nullptr;
-        hipError_t ee = hipStreamEndCapture(m->capture_stream, &graph);
-        if (st != LLAMA_OK) { if (graph) (void)hipGraphDestroy(graph); return st; }
-        if (be != hipSuccess || ee != hipSuccess) {
-            if (graph) (void)hipGraphDestroy(graph);
-            return fail(LLAMA_ERR_HIP, "decode graph capture failed: %s",
-                        hipGetErrorString(be != hipSuccess ? be : ee));
-        }
-        hipError_t ie = hipGraphInstantiate(&m->graph_exec, graph, nullptr, nullptr, 0);
-        (void)hipGraphDestroy(graph);
-        if (ie != hipSuccess) { m->graph_exec = nullptr; return fail(LLAMA_ERR_HIP, "graph instantiate: %s", hipGetErrorString(ie)); }
-        m->graph_B = B;
-        m->graph_max_ctx = cap_ctx;
-        m->graph_out = out_tokens;
-    }
-    for (int k = 0; k < n_steps; ++k) HIP_TRY(hipGraphLaunch(m->graph_exec, s));
     return LLAMA_OK;
 }
 
@@ -470,8 +441,6 @@ llama_status llama_profile_read(llama_model* m, double* total_ms, int32_t* launc
 void llama_free(llama_model* m) {
     if (!m) return;
     for (hipEvent_t e : m->prof_events) (void)hipEventDestroy(e);
-    if (m->graph_exec) (void)hipGraphExecDestroy(m->graph_exec);
-    if (m->capture_stream) (void)hipStreamDestroy(m->capture_stream);
     delete m;
 }
 

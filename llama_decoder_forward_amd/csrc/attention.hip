@@ -305,170 +305,212 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
 // ------------------------------------------------------------------------------------
 // Decode, bf16, head_dim 128: split-K over the cached context on the matrix cores.
 //
-// Workgroup = (split of DEC_CHUNK keys, KV head g, sequence b), 4 waves of 64 keys each.
-// A wave streams its 64 keys of K (16 KB) and V^T (16 KB) straight from HBM into MFMA
-// operand registers (16x16x32 bf16; the `group` query heads of g are the B-operand
-// columns, the rest zero), computes S^T = K Q^T, a local softmax, O^T = V^T P^T, and
-// writes one partial (max, sum, unnormalised o[128]) per query head.  A second kernel
-// merges the partials of every wave that holds at least one key.  Contiguous 64-byte
-// runs per lane: lane quarter kq takes d = 32kq..32kq+31 of each key row (the k index of
-// the MFMA is permuted identically on both operands).
+// Workgroup = (split of the context, KV head g, sequence b), 4 waves.  Each iteration the
+// waves take consecutive 64-key blocks and stream their K (16 KB) and V^T (16 KB) straight
+// from HBM into 16x16x32 MFMA operands, with the `group` query heads of g as the B-operand
+// columns (the rest zero): S^T = K Q^T, an online softmax per head, O^T += V^T P^T.  The
+// four waves' states are merged through LDS and one partial (max, sum, unnormalised o[128])
+// per query head is written; a second kernel merges the splits.
+//
+// Index maps (all 16-byte loads): lane (c = l%16, kq = l/16).  K tile t = 2j + h of a
+// 64-key block holds in MFMA row i the key 32j + 8(i/4) + 4h + i%4, so that the result
+// register e of lane (c, kq) is key 32j + 8kq + 4h + e; the P^T operand of k-step j is then
+// keys 32j + 8kq + 0..7 of the lane's own registers, and the matching V^T operand is one
+// 16-byte run of row d.  Along d, lane kq supplies d = 32kq + 8jj .. +7 for k-step jj.
 // ------------------------------------------------------------------------------------
-constexpr int DEC_KEYS_PER_WAVE = 64;
-constexpr int DEC_CHUNK = 4 * DEC_KEYS_PER_WAVE;  // keys per workgroup (256)
+constexpr int DEC_BLOCK = 64;  // keys per wave per iteration
 
 __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     float* __restrict__ part, int start_pos, const int* pos_dev, int H, int G, int seq_stride,
-    int max_parts, float scale_log2) {
+    int chunk, int max_splits, float scale_log2) {
+    __shared__ float sm_m[4][16], sm_l[4][16];
+    __shared__ f32x4 sm_o[3][8][64];
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int pos = pos_dev ? *pos_dev : start_pos;
     const int ctx = pos + 1;
+    const int c0 = split * chunk;
+    if (c0 >= ctx) return;  // no cached key in this split; the merge skips it
+    const int c1 = min(ctx, c0 + chunk);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int k0 = split * DEC_CHUNK + wave * DEC_KEYS_PER_WAVE;
-    if (k0 >= ctx) return;  // nothing cached here; the merge skips this partial
     const int group = H / G;
     const int col = lane & 15, kq = lane >> 4;
 
-    // B operand Q^T: lane (col, kq) supplies d = 32kq + 8j .. +7 for k-step j
     bf16x8 qf[4];
     {
         const bool real = col < group;
         const bf16* qrow = q + ((size_t)b * H + g * group + (real ? col : 0)) * FA_D + 32 * kq;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            qf[j] = real ? *reinterpret_cast<const bf16x8*>(qrow + 8 * j) : bf16x8{};
+        for (int jj = 0; jj < 4; ++jj)
+            qf[jj] = real ? *reinterpret_cast<const bf16x8*>(qrow + 8 * jj) : bf16x8{};
     }
     const bf16* kbase = kc + ((size_t)b * G + g) * seq_stride * FA_D;
     const bf16* vbase = vc + ((size_t)b * G + g) * FA_D * seq_stride;
 
-    // K: 4 tiles of 16 keys; lane row = key k0 + 16t + col, 64 bytes at d = 32kq
-    u32x4 kr[4][4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        const int key = k0 + 16 * tt + col;
-        const bf16* src = kbase + (size_t)key * FA_D + 32 * kq;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            kr[tt][j] = (key < ctx) ? *reinterpret_cast<const u32x4*>(src + 8 * j) : u32x4{0, 0, 0, 0};
-    }
-    // V^T: 8 tiles of 16 d-rows x 2 k-steps of 32 keys; slot s of lane kq is key
-    // k0 + 32j + 16(s/4) + 4kq + s%4: two 8-byte loads per (tile, step)
-    uint2 vr[8][2][2];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        const bf16* row = vbase + (size_t)(16 * dt + col) * seq_stride;
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const int key = k0 + 32 * j + 16 * h2 + 4 * kq;
-                uint2 v = (key < ctx) ? *reinterpret_cast<const uint2*>(row + key) : make_uint2(0, 0);
-                if (key + 4 > ctx) {  // partial: zero keys >= ctx
-                    if (key + 0 >= ctx) v.x &= 0xFFFF0000u;
-                    if (key + 1 >= ctx) v.x &= 0x0000FFFFu;
-                    if (key + 2 >= ctx) v.y &= 0xFFFF0000u;
-                    if (key + 3 >= ctx) v.y &= 0x0000FFFFu;
-                }
-                vr[dt][j][h2] = v;
-            }
-    }
-
-    // S^T tiles: lane (col, kq) register e of tile t is key k0 + 16t + 4kq + e
-    f32x4 sacc[4];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        sacc[tt] = f32x4{};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, kr[tt][j]), qf[j], sacc[tt], 0, 0, 0);
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int key = k0 + 16 * tt + 4 * kq + e;
-            float sv = sacc[tt][e] * scale_log2;
-            if (key >= ctx) sv = -INFINITY;
-            sacc[tt][e] = sv;
-            mx = fmaxf(mx, sv);
-        }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    float psum = 0.0f;
-    bf16x8 pf[2];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float p = exp2f(sacc[tt][e] - mx);
-            psum += p;
-            pf[tt >> 1][4 * (tt & 1) + e] = from_f32<bf16>(p);
-        }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-
-    // O^T = V^T P^T: 8 d-tiles; lane (col, kq) register e of tile dt is d = 16dt + 4kq + e
+    float m_run = -INFINITY, l_run = 0.0f;
     f32x4 oacc[8];
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-        oacc[dt] = f32x4{};
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{};
+
+    for (int kb = c0 + wave * DEC_BLOCK; kb < c1; kb += 4 * DEC_BLOCK) {
+        u32x4 kr[4][4], vr[8][2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const bf16x8 a = __builtin_bit_cast(
-                bf16x8, u32x4{vr[dt][j][0].x, vr[dt][j][0].y, vr[dt][j][1].x, vr[dt][j][1].y});
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[j], oacc[dt], 0, 0, 0);
+        for (int t = 0; t < 4; ++t) {
+            const int key = kb + 32 * (t >> 1) + 8 * (col >> 2) + 4 * (t & 1) + (col & 3);
+            const bf16* src = kbase + (size_t)key * FA_D + 32 * kq;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                kr[t][jj] = (key < c1) ? *reinterpret_cast<const u32x4*>(src + 8 * jj) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const bf16* row = vbase + (size_t)(16 * dt + col) * seq_stride;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int key = kb + 32 * j + 8 * kq;
+                const u32x4 v = (key < c1) ? *reinterpret_cast<const u32x4*>(row + key) : u32x4{0, 0, 0, 0};
+                vr[dt][j] = mask_keys8(v, key, c1);
+            }
+        }
+        f32x4 sacc[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            sacc[t] = f32x4{};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, kr[t][jj]), qf[jj], sacc[t], 0, 0, 0);
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int key = kb + 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + e;
+                float sv = sacc[t][e] * scale_log2;
+                if (key >= c1) sv = -INFINITY;
+                sacc[t][e] = sv;
+                mx = fmaxf(mx, sv);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float corr = exp2f(m_run - m_new);
+        float psum = 0.0f;
+        bf16x8 pf[2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float p = exp2f(sacc[t][e] - m_new);
+                psum += p;
+                pf[t >> 1][4 * (t & 1) + e] = from_f32<bf16>(p);
+            }
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        l_run = l_run * corr + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            oacc[dt] *= corr;
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, vr[dt][j]), pf[j], oacc[dt], 0, 0, 0);
         }
     }
-    if (col >= group) return;
-    const int h = g * group + col;
-    const int pidx = split * 4 + wave;
-    float* pp = part + ((size_t)(b * H + h) * max_parts + pidx) * (FA_D + 2);
-    if (kq == 0) { pp[0] = mx; pp[1] = psum; }
+
+    // merge the four waves (a wave with no key keeps m = -inf, l = 0, o = 0)
+    if (kq == 0) { sm_m[wave][col] = m_run; sm_l[wave][col] = l_run; }
+    if (wave > 0) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-        *reinterpret_cast<f32x4*>(pp + 2 + 16 * dt + 4 * kq) = oacc[dt];
+        for (int dt = 0; dt < 8; ++dt) sm_o[wave - 1][dt][lane] = oacc[dt];
+    }
+    __syncthreads();
+    if (wave > 0 || col >= group) return;
+    float M = sm_m[0][col];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][col]);
+    float wsc[4], L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        wsc[w] = (sm_m[w][col] == -INFINITY) ? 0.0f : exp2f(sm_m[w][col] - M);
+        L += wsc[w] * sm_l[w][col];
+    }
+    const int h = g * group + col;
+    float* pp = part + ((size_t)(b * H + h) * max_splits + split) * (FA_D + 2);
+    if (kq == 0) { pp[0] = M; pp[1] = L; }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        f32x4 o = oacc[dt] * wsc[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) o += sm_o[w - 1][dt][lane] * wsc[w];
+        *reinterpret_cast<f32x4*>(pp + 2 + 16 * dt + 4 * kq) = o;
+    }
 }
 
-// Merge the partials of one (sequence, head): o = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+// Merge the splits of one (sequence, head): o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 template <typename T>
 __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const float* __restrict__ part,
                                                                 T* __restrict__ out, int start_pos,
                                                                 const int* pos_dev, int H,
-                                                                int d, int max_parts,
-                                                                int keys_per_part) {
+                                                                int d, int max_splits, int chunk) {
+    __shared__ float wts[128];
+    __shared__ float red[2];
     const int h = blockIdx.x, b = blockIdx.y;
     const int pos = pos_dev ? *pos_dev : start_pos;
-    const int nparts = (pos + 1 + keys_per_part - 1) / keys_per_part;
-    const float* pp = part + (size_t)(b * H + h) * max_parts * (d + 2);
-    float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, pp[(size_t)p * (d + 2)]);
-    for (int i = threadIdx.x; i < d; i += blockDim.x) {
-        float num = 0.0f, den = 0.0f;
-        for (int p = 0; p < nparts; ++p) {
-            const float* q = pp + (size_t)p * (d + 2);
-            const float w = exp2f(q[0] - M);
-            den += w * q[1];
-            num += w * q[2 + i];
-        }
+    const int nsplit = (pos + 1 + chunk - 1) / chunk;  // <= 128
+    const float* pp = part + (size_t)(b * H + h) * max_splits * (d + 2);
+    const int t = threadIdx.x;
+    const float mt = t < nsplit ? pp[(size_t)t * (d + 2)] : -INFINITY;
+    wts[t] = mt;
+    __syncthreads();
+    if (t == 0) {
+        float M = -INFINITY;
+        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wts[s]);
+        red[0] = M;
+    }
+    __syncthreads();
+    const float w = t < nsplit ? exp2f(mt - red[0]) : 0.0f;
+    const float lw = t < nsplit ? w * pp[(size_t)t * (d + 2) + 1] : 0.0f;
+    __syncthreads();
+    wts[t] = w;
+    const float lsum = wave_sum(lw);
+    if ((t & 63) == 0) red[t >> 6] = lsum;  // red[0] (the max) is no longer needed
+    __syncthreads();
+    const float den = red[0] + red[1];
+    for (int i = t; i < d; i += blockDim.x) {
+        float num = 0.0f;
+        for (int s = 0; s < nsplit; ++s) num += wts[s] * pp[(size_t)s * (d + 2) + 2 + i];
         out[(size_t)b * H * d + (size_t)h * d + i] = from_f32<T>(num / den);
     }
 }
 
+// keys per split: enough workgroups (about 1024) to keep every CU streaming, at most 128
+// splits for the merge
+int decode_chunk(const AttnArgs& a) {
+    int chunk = 4 * DEC_BLOCK;
+    while (chunk < 16 * 4 * DEC_BLOCK) {
+        const long long splits = (a.max_ctx + chunk - 1) / chunk;
+        if (splits * a.G * a.B <= 2048 && splits <= 128) break;
+        chunk *= 2;
+    }
+    while ((a.max_ctx + chunk - 1) / chunk > 128) chunk *= 2;
+    return chunk;
+}
+
 hipError_t launch_decode_mfma(const AttnArgs& a, hipStream_t s) {
-    const int splits = (a.max_ctx + DEC_CHUNK - 1) / DEC_CHUNK;
-    const int max_parts = a.seq_stride / DEC_KEYS_PER_WAVE;
+    const int chunk = decode_chunk(a);
+    const int splits = (a.max_ctx + chunk - 1) / chunk;
+    const int max_splits = (a.seq_stride + 4 * DEC_BLOCK - 1) / (4 * DEC_BLOCK);
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_D);
     attn_decode_mfma_kernel<<<dim3(splits, a.G, a.B), 256, 0, s>>>(
         (const bf16*)a.q, (const bf16*)a.kc, (const bf16*)a.vc, a.partials, a.start_pos,
-        a.pos_dev, a.H, a.G, a.seq_stride, max_parts, scale_log2);
+        a.pos_dev, a.H, a.G, a.seq_stride, chunk, max_splits, scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     attn_decode_merge_kernel<bf16><<<dim3(a.H, a.B), 128, 0, s>>>(
-        a.partials, (bf16*)a.out, a.start_pos, a.pos_dev, a.H, FA_D, max_parts,
-        DEC_KEYS_PER_WAVE);
+        a.partials, (bf16*)a.out, a.start_pos, a.pos_dev, a.H, FA_D, max_splits, chunk);
     return hipGetLastError();
 }
 

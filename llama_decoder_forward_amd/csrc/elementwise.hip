@@ -118,53 +118,86 @@ hipError_t rmsnorm(Dt dt, const float* x, int in_row_step, int in_row_offset, co
 }
 
 // Greedy choice per row: the largest logit, lowest index among equals (article, section
-// 预测下一个输出, torch.argmax).  NaN raises DEVERR_NAN_LOGIT.  Writes out[r]; if out2 is
-// set also out2[(*counter) * out2_step + r] (the generated-token log of a decode loop).
-__global__ __launch_bounds__(1024) void argmax_kernel(const float* logits, int V, int* out,
-                                                      int* out2, int out2_step,
-                                                      const int* counter, uint32_t* err) {
-    const int r = blockIdx.x;
+// 预测下一个输出, torch.argmax).  NaN raises DEVERR_NAN_LOGIT.  Two stages: blocks of
+// ARGMAX_CHUNK logits each write their (max, index), then one wave per row reduces them and
+// writes out[r] and, if out2 is set, out2[(*counter) * out2_step + r] (the token log of a
+// decode loop).
+constexpr int ARGMAX_CHUNK = 4096;
+
+__device__ __forceinline__ void better(float& best, int& idx, float v, int i) {
+    if (v > best || (v == best && i < idx)) { best = v; idx = i; }
+}
+
+__global__ __launch_bounds__(256) void argmax_partial_kernel(const float* logits, int V,
+                                                             float* pv, int* pi, int nchunks,
+                                                             uint32_t* err) {
+    const int c = blockIdx.x, r = blockIdx.y;
     const float* lr = logits + (size_t)r * V;
+    const int lo = c * ARGMAX_CHUNK, hi = min(V, lo + ARGMAX_CHUNK);
     float best = -INFINITY;
     int idx = 0x7fffffff;
     bool nan = false;
-    for (int i = threadIdx.x; i < V; i += blockDim.x) {
+    for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
         const float v = lr[i];
-        if (v != v) nan = true;
-        if (v > best || (v == best && i < idx)) { best = v; idx = i; }
+        nan |= (v != v);
+        better(best, idx, v, i);
     }
-    // wave reduce
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         const float ob = __shfl_xor(best, o, WAVE);
         const int oi = __shfl_xor(idx, o, WAVE);
-        if (ob > best || (ob == best && oi < idx)) { best = ob; idx = oi; }
+        better(best, idx, ob, oi);
     }
-    __shared__ float sb[16];
-    __shared__ int si[16];
-    __shared__ int snan;
-    if (threadIdx.x == 0) snan = 0;
-    __syncthreads();
-    if (nan) snan = 1;
+    __shared__ float sb[4];
+    __shared__ int si[4];
+    if (nan) atomicOr(err, DEVERR_NAN_LOGIT);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) { sb[w] = best; si[w] = idx; }
     __syncthreads();
     if (threadIdx.x == 0) {
-        float b = sb[0];
-        int ix = si[0];
-        for (int k = 1; k < (int)(blockDim.x >> 6); ++k)
-            if (sb[k] > b || (sb[k] == b && si[k] < ix)) { b = sb[k]; ix = si[k]; }
-        if (snan) { atomicOr(err, DEVERR_NAN_LOGIT); ix = 0; }
-        if (ix == 0x7fffffff) ix = 0;  // all -inf
-        out[r] = ix;
-        if (out2) out2[(size_t)(*counter) * out2_step + r] = ix;
+        best = sb[0]; idx = si[0];
+        for (int k = 1; k < 4; ++k) better(best, idx, sb[k], si[k]);
+        pv[(size_t)r * nchunks + c] = best;
+        pi[(size_t)r * nchunks + c] = idx;
     }
 }
 
+__global__ __launch_bounds__(64) void argmax_final_kernel(const float* pv, const int* pi,
+                                                          int nchunks, int* out, int* out2,
+                                                          int out2_step, const int* counter) {
+    const int r = blockIdx.x;
+    float best = -INFINITY;
+    int idx = 0x7fffffff;
+    for (int c = threadIdx.x; c < nchunks; c += 64)
+        better(best, idx, pv[(size_t)r * nchunks + c], pi[(size_t)r * nchunks + c]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ob = __shfl_xor(best, o, WAVE);
+        const int oi = __shfl_xor(idx, o, WAVE);
+        better(best, idx, ob, oi);
+    }
+    if (threadIdx.x == 0) {
+        if (idx == 0x7fffffff) idx = 0;  // all -inf or NaN
+        out[r] = idx;
+        if (out2) out2[(size_t)(*counter) * out2_step + r] = idx;
+    }
+}
+
+size_t argmax_scratch_bytes(int rows, int V) {
+    const size_t nchunks = (V + ARGMAX_CHUNK - 1) / ARGMAX_CHUNK;
+    return (size_t)rows * nchunks * 8;
+}
+
 hipError_t argmax(const float* logits, int rows, int V, int* out, int* out2, int out2_step,
-                  const int* counter, uint32_t* err, hipStream_t s) {
+                  const int* counter, void* scratch, uint32_t* err, hipStream_t s) {
     if (rows == 0) return hipSuccess;
-    argmax_kernel<<<rows, 1024, 0, s>>>(logits, V, out, out2, out2_step, counter, err);
+    const int nchunks = (V + ARGMAX_CHUNK - 1) / ARGMAX_CHUNK;
+    float* pv = static_cast<float*>(scratch);
+    int* pi = reinterpret_cast<int*>(pv + (size_t)rows * nchunks);
+    argmax_partial_kernel<<<dim3(nchunks, rows), 256, 0, s>>>(logits, V, pv, pi, nchunks, err);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    argmax_final_kernel<<<rows, 64, 0, s>>>(pv, pi, nchunks, out, out2, out2_step, counter);
     return hipGetLastError();
 }
 

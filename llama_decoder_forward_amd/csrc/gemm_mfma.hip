@@ -163,6 +163,7 @@ hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
 template <bool DUAL, typename Epi>
 hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
+    if (skinny_ok(g)) return skinny_launch<DUAL>(g, e, s);
     if (g.M <= 32) return launch_cfg<128, 32, 4, 1, DUAL>(g, e, s);
     return launch_cfg<128, 128, 2, 2, DUAL>(g, e, s);
 }

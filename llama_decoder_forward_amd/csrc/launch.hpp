@@ -14,8 +14,9 @@ hipError_t embed(Dt dt, const int* tokens, const void* E, float* x, int rows, in
 // y[r] = rmsnorm(x[r * in_stride_rows + in_offset_rows]) for r < rows
 hipError_t rmsnorm(Dt dt, const float* x, int in_row_step, int in_row_offset, const void* w,
                    void* y, int rows, int D, float eps, hipStream_t s);
+size_t argmax_scratch_bytes(int rows, int V);
 hipError_t argmax(const float* logits, int rows, int V, int* out, int* out2, int out2_step,
-                  const int* counter, uint32_t* err, hipStream_t s);
+                  const int* counter, void* scratch, uint32_t* err, hipStream_t s);
 hipError_t bump_counters(int* pos, int* step, hipStream_t s);
 hipError_t zero_u32(uint32_t* p, int n, hipStream_t s);
 hipError_t copy_tokens(const int* src, int* dst, int n, hipStream_t s);
@@ -28,6 +29,10 @@ template <typename T> struct GemmArgs {
     WeightRows<T> W3;  // second weight set of the SwiGLU gate/up GEMM
     int M, N, K;
 };
+// weight-streaming path for few rows (gemm_skinny.hip)
+bool skinny_ok(const GemmArgs<void>& g);
+template <bool DUAL, typename Epi>
+hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s);
 hipError_t gemm_store_f32(Dt dt, const GemmArgs<void>& g, EpiStoreF32 e, hipStream_t s);
 hipError_t gemm_residual(Dt dt, const GemmArgs<void>& g, EpiResidual e, hipStream_t s);
 hipError_t gemm_swiglu(Dt dt, const GemmArgs<void>& g, void* out, int ld, hipStream_t s);
