@@ -101,7 +101,7 @@ def main() -> int:
     ap.add_argument("--seq", type=int, default=2048)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=8)
+    ap.add_argument("--cpu-layers", type=int, default=10)
     ap.add_argument("--profile-only", action="store_true",
                     help="a short run for rocprofv3: 1 warmup + --steps prefill, 8 decode steps")
     args = ap.parse_args()

@@ -22,56 +22,82 @@ hipError_t simt_qkv(const GemmArgs<void>& g, const EpiQKV<void>& e, hipStream_t 
 
 namespace {
 
-constexpr int BK = 64;
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane i
+// of the wave writes LDS bytes [lds + 16 i, lds + 16 i + 16).  Issued from inline asm so
+// that the compiler does not serialise every later LDS read behind it; completion is
+// tracked by hand with s_waitcnt vmcnt (the copy has no VGPR result).
+__device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds_byte) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "v"(gptr)
+                 : "memory");
+}
 
-template <int BN, int BM, int WN, int WM, bool DUAL, typename Epi>
+template <int N>
+__device__ __forceinline__ void wait_vm_and_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+// Block tile BN weight rows x BM tokens x BK, STAGES-deep LDS ring.  LDS row = BK bf16
+// (RB bytes) split in 16-byte chunks; chunk c of row r is stored at c ^ swz(r) so that the
+// MFMA operand reads of consecutive rows hit distinct banks.
+template <int BN, int BM, int BK, int STAGES, int WN, int WM, bool DUAL, typename Epi>
 __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
     const bf16* __restrict__ A, int lda, WeightRows<bf16> W, WeightRows<bf16> W3, int M, int N,
     int K, Epi epi) {
-    constexpr int NT = WN * WM * 64;
+    constexpr int NW = WN * WM;
     constexpr int NA = DUAL ? 2 : 1;
-    constexpr int ROWS = NA * BN + BM;       // rows of one LDS stage (64 bf16 = 8 chunks each)
-    constexpr int CH = ROWS * 8 / NT;        // 16-byte chunks loaded per thread per stage
+    constexpr int ROWS = NA * BN + BM;
+    constexpr int RB = BK * 2;                 // bytes per LDS row
+    constexpr int CPR = RB / 16;               // 16-byte chunks per row
+    constexpr int STAGE = ROWS * RB;           // bytes per stage
+    constexpr int SPW = STAGE / 1024 / NW;     // 1 KB copies per wave per stage
     constexpr int TN = BN / WN / 32, TM = BM / WM / 32;
-    static_assert(ROWS * 8 % NT == 0, "tile/thread mismatch");
-    extern __shared__ u32x4 lds[];           // [2][ROWS * 8]
+    static_assert(STAGE % (1024 * NW) == 0, "stage must split into whole 1 KB copies per wave");
+    static_assert((STAGES - 2) * SPW < 64, "vmcnt range");
+    extern __shared__ u32x4 lds[];
+
+    // 8 consecutive rows (one 128-byte bank window) and 16 consecutive rows (a 256-byte one)
+    // both land on distinct 16-byte slots
+    auto swz = [](int r) {
+        return CPR == 8 ? (((r >> 1) ^ (r << 2)) & 7) : (((r >> 1) ^ (r >> 3)) & 3);
+    };
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wn = wave / WM, wm = wave % WM;
-    const int nt_m = (M + BM - 1) / BM;
-    const int tile_m = blockIdx.x % nt_m, tile_n = blockIdx.x / nt_m;
+    const int nt_m = (M + BM - 1) / BM, nt_n = (N + BN - 1) / BN;
+    const int tiles = nt_m * nt_n;
+    int bid = blockIdx.x;
+    // workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous run of
+    // tiles (token tiles fastest) so that tiles sharing weight rows share that XCD's L2
+    if (tiles % 8 == 0) bid = (bid & 7) * (tiles >> 3) + (bid >> 3);
+    const int tile_m = bid % nt_m, tile_n = bid / nt_m;
     const int n0 = tile_n * BN, m0 = tile_m * BM;
 
-    // each thread loads chunk (t & 7) of rows (t >> 3) + i * NT/8
-    const int c = t & 7;
-    const bf16* src[CH];
-    int row_of[CH];
+    // this lane's source address for each of its wave's copies of a stage
+    const bf16* src[SPW];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-        const int r = (t >> 3) + i * (NT / 8);
-        row_of[i] = r;
-        const bf16* p = nullptr;
+    for (int i = 0; i < SPW; ++i) {
+        const int byte = (wave + i * NW) * 1024 + lane * 16;
+        const int r = byte / RB, pc = (byte % RB) / 16;
+        const int c = pc ^ swz(r);
+        const bf16* p;
         if (r < BN) {
-            if (n0 + r < N) p = W.row(n0 + r);
+            p = W.row(n0 + r < N ? n0 + r : 0);
         } else if (DUAL && r < 2 * BN) {
-            if (n0 + r - BN < N) p = W3.row(n0 + r - BN);
+            p = W3.row(n0 + r - BN < N ? n0 + r - BN : 0);
         } else {
             const int m = m0 + r - NA * BN;
-            if (m < M) p = A + (size_t)m * lda;
+            p = A + (size_t)(m < M ? m : 0) * lda;   // rows past M / N load row 0, unused
         }
-        src[i] = p ? p + c * 8 : nullptr;
+        src[i] = p + c * 8;
     }
-
-    u32x4 regs[CH];
-    auto gload = [&](int k0) {
+    // LDS byte offset of the ring (address-space cast from the generic pointer)
+    const unsigned lds0 = (unsigned)(uintptr_t)((__attribute__((address_space(3))) const void*)lds);
+    auto issue = [&](int st, int k0) {
 #pragma unroll
-        for (int i = 0; i < CH; ++i)
-            regs[i] = src[i] ? *reinterpret_cast<const u32x4*>(src[i] + k0) : u32x4{0, 0, 0, 0};
-    };
-    auto swrite = [&](int st) {
-        u32x4* base = lds + st * ROWS * 8;
-#pragma unroll
-        for (int i = 0; i < CH; ++i) base[row_of[i] * 8 + (c ^ (row_of[i] & 7))] = regs[i];
+        for (int i = 0; i < SPW; ++i)
+            lds_dma16(src[i] + k0, lds0 + st * STAGE + (wave + i * NW) * 1024);
     };
 
     f32x16 acc[TN][TM];
@@ -86,36 +112,56 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
 
     const int lr = lane & 31, lh = lane >> 5;
     const int nk = K / BK;
-    gload(0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const int st = kt & 1;
-        swrite(st);
-        __syncthreads();
-        if (kt + 1 < nk) gload((kt + 1) * BK);
-        const u32x4* base = lds + st * ROWS * 8;
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int ch = (kk * 2 + lh) ^ (lr & 7);
-            bf16x8 a[TN], a3[DUAL ? TN : 1], b[TM];
+    for (int st = 0; st < STAGES - 1; ++st)
+        if (st < nk) issue(st, st * BK);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        // tile kt has landed once at most the copies of the later tiles are outstanding
+        if (kt + STAGES - 2 < nk) wait_vm_and_barrier<(STAGES - 2) * SPW>();
+        else wait_vm_and_barrier<0>();
+        if (kt + STAGES - 1 < nk) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
+        const char* base = reinterpret_cast<const char*>(lds) + (kt % STAGES) * STAGE;
+        // fragments of k-step kk+1 are read from LDS while the MFMAs of step kk run
+        bf16x8 fa[2][TN], fa3[2][DUAL ? TN : 1], fb[2][TM];
+        auto frags = [&](int buf, int kk) {
+            const int ch = kk * 2 + lh;
 #pragma unroll
             for (int i = 0; i < TN; ++i) {
                 const int r = wn * (BN / WN) + i * 32 + lr;
-                a[i] = __builtin_bit_cast(bf16x8, base[r * 8 + ch]);
-                if constexpr (DUAL) a3[i] = __builtin_bit_cast(bf16x8, base[(BN + r) * 8 + ch]);
+                fa[buf][i] = *reinterpret_cast<const bf16x8*>(base + r * RB + (ch ^ swz(r)) * 16);
+                if constexpr (DUAL)
+                    fa3[buf][i] = *reinterpret_cast<const bf16x8*>(base + (BN + r) * RB + (ch ^ swz(BN + r)) * 16);
             }
 #pragma unroll
             for (int j = 0; j < TM; ++j) {
                 const int r = NA * BN + wm * (BM / WM) + j * 32 + lr;
-                b[j] = __builtin_bit_cast(bf16x8, base[r * 8 + ch]);
+                fb[buf][j] = *reinterpret_cast<const bf16x8*>(base + r * RB + (ch ^ swz(r)) * 16);
             }
+        };
+        frags(0, 0);
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            const int cur = kk & 1;
+            if (kk + 1 < BK / 16) frags(cur ^ 1, kk + 1);
 #pragma unroll
             for (int i = 0; i < TN; ++i)
 #pragma unroll
                 for (int j = 0; j < TM; ++j) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
                     if constexpr (DUAL)
-                        acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i], b[j], acc3[i][j], 0, 0, 0);
+                        acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa3[cur][i], fb[cur][j], acc3[i][j], 0, 0, 0);
                 }
+            if (kk + 1 < BK / 16) {
+                // interleave: one LDS read after each MFMA, then the remaining MFMAs
+                constexpr int NREAD = NA * TN + TM, NMFMA = NA * TN * TM;
+#pragma unroll
+                for (int q = 0; q < NREAD; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
+            }
         }
     }
 
@@ -139,16 +185,20 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
                     epi(m, n, v);
                 }
             }
+            // one 32x32 tile at a time: keeps the epilogue's loads from raising the kernel's
+            // register count (and so its occupancy)
+            __builtin_amdgcn_sched_barrier(0);
         }
 }
 
-template <int BN, int BM, int WN, int WM, bool DUAL, typename Epi>
+template <int BN, int BM, int BK, int STAGES, int WN, int WM, bool DUAL, typename Epi>
 hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     const WeightRows<bf16> W{(const bf16*)g.W.p0, (const bf16*)g.W.p1, (const bf16*)g.W.p2, g.W.end0, g.W.end1, g.W.ld};
     const WeightRows<bf16> W3{(const bf16*)g.W3.p0, (const bf16*)g.W3.p1, (const bf16*)g.W3.p2, g.W3.end0, g.W3.end1, g.W3.ld};
     constexpr int ROWS = (DUAL ? 2 : 1) * BN + BM;
-    constexpr size_t lds_bytes = 2 * ROWS * 8 * sizeof(u32x4);
-    auto kern = gemm_mfma_kernel<BN, BM, WN, WM, DUAL, Epi>;
+    constexpr size_t lds_bytes = (size_t)STAGES * ROWS * BK * 2;
+    static_assert(lds_bytes <= 160 * 1024, "LDS");
+    auto kern = gemm_mfma_kernel<BN, BM, BK, STAGES, WN, WM, DUAL, Epi>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
@@ -160,12 +210,24 @@ hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Tile shapes per GEMM shape, measured on MI355X (8B-shaped layer at 2048 and 32768 tokens):
+//  - wide weight matrices (Q/K/V, the vocabulary) and every GEMM with many token tiles:
+//    256 x 256 macro tile, 8 waves of 128 x 64, two 64-deep LDS stages;
+//  - the SwiGLU gate/up pair: 128 rows of W1 + 128 of W3 against 256 tokens, 8 waves;
+//  - N = dim outputs (WO, W2) at a few thousand tokens: 128 x 128, 4 waves, so that the
+//    grid still covers the 256 CUs.
 template <bool DUAL, typename Epi>
 hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
     if (skinny_ok(g)) return skinny_launch<DUAL>(g, e, s);
-    if (g.M <= 32) return launch_cfg<128, 32, 4, 1, DUAL>(g, e, s);
-    return launch_cfg<128, 128, 2, 2, DUAL>(g, e, s);
+    if (g.M <= 32) return launch_cfg<128, 32, 64, 3, 4, 1, DUAL>(g, e, s);
+    if constexpr (DUAL) {
+        return launch_cfg<128, 256, 64, 2, 2, 4, DUAL>(g, e, s);
+    } else {
+        const long long tiles256 = (long long)((g.N + 255) / 256) * ((g.M + 255) / 256);
+        if (g.N >= 6144 || tiles256 >= 512) return launch_cfg<256, 256, 64, 2, 2, 4, DUAL>(g, e, s);
+        return launch_cfg<128, 128, 64, 2, 2, 2, DUAL>(g, e, s);
+    }
 }
 
 }  // namespace

@@ -179,13 +179,16 @@ template <bool DUAL, typename Epi>
 hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     const bool wide = g.N >= 16384;
     if (g.M <= 16) return launch_mb<1, 1, DUAL>(g, e, s);
-    if (g.M <= 32) {
-        if (DUAL && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 2, DUAL>(g, e, s);
-        if (!DUAL && wide && g.N % (SK_ROWS * 4) == 0) return launch_mb<4, 2, DUAL>(g, e, s);
-        return launch_mb<1, 2, DUAL>(g, e, s);
+    if constexpr (DUAL) {
+        if (g.M <= 32 && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 2, DUAL>(g, e, s);
+        if (g.M <= 32) return launch_mb<1, 2, DUAL>(g, e, s);
+        return launch_mb<1, 4, DUAL>(g, e, s);
+    } else {
+        if (g.M <= 32 && wide && g.N % (SK_ROWS * 4) == 0) return launch_mb<4, 2, DUAL>(g, e, s);
+        if (g.M <= 32) return launch_mb<1, 2, DUAL>(g, e, s);
+        if (wide && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 4, DUAL>(g, e, s);
+        return launch_mb<1, 4, DUAL>(g, e, s);
     }
-    if (!DUAL && wide && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 4, DUAL>(g, e, s);
-    return launch_mb<1, 4, DUAL>(g, e, s);
 }
 
 template hipError_t skinny_launch<false, EpiStoreF32>(const GemmArgs<void>&, const EpiStoreF32&, hipStream_t);
