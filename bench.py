@@ -54,6 +54,45 @@ def decode_bytes(spec, B: int, ctx_first: int, steps: int) -> float:
     return total
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILES = {
+    "ffn_up": os.path.join(ROOT, "profiles", "ffn_up_gemm_8b_prefill_s2048_traffic.txt"),
+    "attention_decode": os.path.join(ROOT, "profiles", "decode_attention_8b_b32_ctx4096_traffic.txt"),
+}
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources; a traffic figure is only reported for the sources it
+    was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "llama_decoder_forward_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or
+    None if there is none or the kernel sources changed since it was taken."""
+    path = TRAFFIC_FILES[kind]
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(spec, seed: int, S: int, n_layers_sample: int):
     """Time the CPU oracle (float32) on `n_layers_sample` of the 32 layers of the prefill
     at S tokens plus the head; scale the per-layer time to the whole stack."""
@@ -102,10 +141,16 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=10)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--print-source-hash", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="a short run for rocprofv3: 1 warmup + --steps prefill, 8 decode steps")
     args = ap.parse_args()
 
+    if args.print_source_hash:
+        print(kernel_source_hash())
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -119,6 +164,13 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copied 1 GiB (1073741824 bytes) device to device for counter calibration")
+        del src, dst
     spec = syn.LLAMA3_8B
     seed = 3
     dec_B, dec_ctx, dec_steps = args.decode_batch, args.decode_ctx, args.decode_steps
@@ -182,7 +234,8 @@ def main() -> int:
         "prefill_tflops": flops / (ms_step * 1e-3) / 1e12,
         "roofline": {"kernel": "ffn_up (W1/W3 GEMM + SiLU*up), M=2048 N=2x14336 K=4096",
                      "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                     "traffic": measured_traffic("ffn_up"),
                      "avg_launch_ms": k_avg, "launches": k_n},
     }
 
@@ -227,7 +280,8 @@ def main() -> int:
             "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "roofline": {"kernel": "decode attention (split-K over the cache)", "bound": "hbm",
                          "achieved": a_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": a_gbs / PEAK_HBM_GBS, "traffic": None,
+                         "frac": a_gbs / PEAK_HBM_GBS,
+                         "traffic": measured_traffic("attention_decode"),
                          "avg_launch_ms": a_avg, "launches": a_n},
             "tokens_head": out[:4, 0].tolist(),
         }

@@ -25,6 +25,13 @@ to float arrays stored [out, in], used as ``x @ W.T``.
 
 Parity pins: every function is pinned by tests that do not call it to check itself
 (printed values, closed forms, library special cases, brute force); see tests/.
+
+Optional bf16 storage-point emulation (``bf16_points=True``): the values a bf16 inference
+path stores in bfloat16 (the normalised GEMM inputs, q, the cached k and v, the softmax
+probabilities the article casts to bf16 in its head loop, the attention output, the
+feed-forward hidden state) are rounded to bfloat16 where they are produced.  It is a
+diagnostic used to size the expected gap between a bf16 path and this float reference;
+it is never the reference itself.
 """
 from __future__ import annotations
 
@@ -49,6 +56,26 @@ def ffn_hidden_size(dim: int, multiple_of: int, ffn_dim_multiplier: float | None
     if ffn_dim_multiplier is not None:
         hidden = int(ffn_dim_multiplier * hidden)
     return multiple_of * ((hidden + multiple_of - 1) // multiple_of)
+
+
+# ---------------------------------------------------------------------------------------
+# bfloat16 rounding (diagnostic emulation only)
+# ---------------------------------------------------------------------------------------
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 value (ties to even) and return it in x's float type.
+
+    bfloat16 keeps the top 16 bits of a float32; rounding adds 0x7FFF plus the lowest kept
+    bit before truncating.  Done on a float32 view; NaN/Inf are not expected here.
+    """
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.asarray(x).dtype)
+
+
+def _maybe_bf16(x: np.ndarray, on: bool) -> np.ndarray:
+    return round_bf16(x) if on else x
 
 
 # ---------------------------------------------------------------------------------------
@@ -125,7 +152,7 @@ def softmax(scores: np.ndarray) -> np.ndarray:
 
 
 def causal_gqa_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
-                         query_positions: np.ndarray) -> np.ndarray:
+                         query_positions: np.ndarray, bf16_points: bool = False) -> np.ndarray:
     """Grouped-query causal attention for one sequence.
 
     q: [S, H, d] (rotated); keys, values: [G, ctx, d] (keys rotated), holding positions
@@ -144,7 +171,7 @@ def causal_gqa_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
     for head in range(H):
         kv = head // group
         scores = (q[:, head, :] @ keys[kv].T) / math.sqrt(d)
-        probs = softmax(scores + mask)
+        probs = _maybe_bf16(softmax(scores + mask), bf16_points)
         out[:, head, :] = probs @ values[kv]
     return out
 
@@ -182,7 +209,7 @@ class SequenceCache:
 
 
 def layer_forward(x: np.ndarray, weights, cfg, layer: int, cache: SequenceCache,
-                  start_pos: int) -> np.ndarray:
+                  start_pos: int, bf16_points: bool = False) -> np.ndarray:
     """One decoder layer for the S tokens of one sequence at positions start_pos..start_pos+S-1.
 
     Article, sections 构建Transformer层 through 前馈神经网络层, in order:
@@ -200,23 +227,28 @@ def layer_forward(x: np.ndarray, weights, cfg, layer: int, cache: SequenceCache,
     W = lambda name: np.asarray(weights[p + name], dtype=dt)  # noqa: E731
 
     positions = start_pos + np.arange(S)
-    h = rms_norm(x, W("attention_norm.weight"), cfg.norm_eps)
+    b16 = bf16_points
+    h = _maybe_bf16(rms_norm(x, W("attention_norm.weight"), cfg.norm_eps), b16)
     q = (h @ W("attention.wq.weight").T).reshape(S, H, d)
     k = (h @ W("attention.wk.weight").T).reshape(S, G, d)
-    v = (h @ W("attention.wv.weight").T).reshape(S, G, d)
-    q = rope_rotate(q, positions, cfg.rope_theta)
-    k = rope_rotate(k, positions, cfg.rope_theta)
+    v = _maybe_bf16((h @ W("attention.wv.weight").T).reshape(S, G, d), b16)
+    q = _maybe_bf16(rope_rotate(q, positions, cfg.rope_theta), b16)
+    k = _maybe_bf16(rope_rotate(k, positions, cfg.rope_theta), b16)
 
     cache.k[layer][:, start_pos:start_pos + S, :] = k.transpose(1, 0, 2)
     cache.v[layer][:, start_pos:start_pos + S, :] = v.transpose(1, 0, 2)
     ctx = start_pos + S
     attn = causal_gqa_attention(q, cache.k[layer][:, :ctx, :], cache.v[layer][:, :ctx, :],
-                                positions)
+                                positions, bf16_points=b16)
 
-    x = x + attn.reshape(S, H * d) @ W("attention.wo.weight").T
-    h2 = rms_norm(x, W("ffn_norm.weight"), cfg.norm_eps)
-    x = x + swiglu_ffn(h2, W("feed_forward.w1.weight"), W("feed_forward.w3.weight"),
-                       W("feed_forward.w2.weight"))
+    x = x + _maybe_bf16(attn.reshape(S, H * d), b16) @ W("attention.wo.weight").T
+    h2 = _maybe_bf16(rms_norm(x, W("ffn_norm.weight"), cfg.norm_eps), b16)
+    if b16:
+        g = round_bf16(silu(h2 @ W("feed_forward.w1.weight").T) * (h2 @ W("feed_forward.w3.weight").T))
+        x = x + g @ W("feed_forward.w2.weight").T
+    else:
+        x = x + swiglu_ffn(h2, W("feed_forward.w1.weight"), W("feed_forward.w3.weight"),
+                           W("feed_forward.w2.weight"))
     return x
 
 
@@ -229,15 +261,17 @@ def embed(tokens: np.ndarray, weights, dtype=np.float64) -> np.ndarray:
     return np.asarray(weights["tok_embeddings.weight"], dtype=dtype)[np.asarray(tokens)]
 
 
-def head_logits(x: np.ndarray, weights, cfg) -> np.ndarray:
+def head_logits(x: np.ndarray, weights, cfg, bf16_points: bool = False) -> np.ndarray:
     """Final RMSNorm, applied once, then the output projection to vocabulary logits
     (article, section 预测下一个输出)."""
     y = rms_norm(x, np.asarray(weights["norm.weight"], dtype=x.dtype), cfg.norm_eps)
+    y = _maybe_bf16(y, bf16_points)
     return y @ np.asarray(weights["output.weight"], dtype=x.dtype).T
 
 
 def prefill_sequence(tokens: np.ndarray, weights, cfg, cache: SequenceCache,
-                     all_positions: bool = False, dtype=np.float64) -> np.ndarray:
+                     all_positions: bool = False, dtype=np.float64,
+                     bf16_points: bool = False) -> np.ndarray:
     """Causal prefill of one sequence from position 0.
 
     Returns the logits of the last position [V], or of every position [S, V]
@@ -246,10 +280,10 @@ def prefill_sequence(tokens: np.ndarray, weights, cfg, cache: SequenceCache,
     """
     x = embed(tokens, weights, dtype)
     for layer in range(cfg.n_layers):
-        x = layer_forward(x, weights, cfg, layer, cache, start_pos=0)
+        x = layer_forward(x, weights, cfg, layer, cache, start_pos=0, bf16_points=bf16_points)
     if all_positions:
-        return head_logits(x, weights, cfg)
-    return head_logits(x[-1:], weights, cfg)[0]
+        return head_logits(x, weights, cfg, bf16_points)
+    return head_logits(x[-1:], weights, cfg, bf16_points)[0]
 
 
 def decode_sequence_step(token: int, pos: int, weights, cfg, cache: SequenceCache,
@@ -272,15 +306,15 @@ def argmax(logits: np.ndarray) -> np.ndarray:
 
 
 def prefill(tokens: np.ndarray, weights, cfg, capacity: int | None = None,
-            all_positions: bool = False, dtype=np.float64):
+            all_positions: bool = False, dtype=np.float64, bf16_points: bool = False):
     """Batch prefill: each row of ``tokens`` [B, S] is an independent sequence.
 
     Returns (logits [B, V] or [B, S, V], list of per-row caches)."""
     tokens = np.asarray(tokens)
     B, S = tokens.shape
     caches = [SequenceCache(cfg, capacity or S, dtype) for _ in range(B)]
-    logits = np.stack([prefill_sequence(tokens[b], weights, cfg, caches[b], all_positions, dtype)
-                       for b in range(B)])
+    logits = np.stack([prefill_sequence(tokens[b], weights, cfg, caches[b], all_positions, dtype,
+                                        bf16_points) for b in range(B)])
     return logits, caches
 
 

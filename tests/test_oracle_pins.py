@@ -330,6 +330,30 @@ def test_one_8b_layer_shapes_float32():
     assert np.isfinite(y).all()
 
 
+# ------------------------------------------------------------------ bf16 emulation (diagnostic)
+
+def test_round_bf16_matches_torch_library():
+    rng = _rng(9)
+    x = np.concatenate([rng.standard_normal(10000) * 10.0 ** rng.integers(-8, 8, 10000),
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0, -0.0])])
+    x32 = x.astype(np.float32)
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(O.round_bf16(x32), ref)
+    np.testing.assert_array_equal(O.round_bf16(ref), ref)  # idempotent on bf16 values
+
+
+def test_bf16_emulation_is_off_by_default_and_small():
+    cfg = syn.TINY
+    W = syn.FloatView(syn.SyntheticWeights(cfg, seed=1))
+    toks = syn.tokens(1, 1, 17, cfg.vocab_size)
+    a, _ = O.prefill(toks, W, cfg, all_positions=True)
+    b, _ = O.prefill(toks, W, cfg, all_positions=True, bf16_points=False)
+    c, _ = O.prefill(toks, W, cfg, all_positions=True, bf16_points=True)
+    np.testing.assert_array_equal(a, b)
+    rel = np.max(np.abs(c - a), -1) / np.max(np.abs(a), -1)
+    assert 0 < rel.max() < 2e-2
+
+
 # ------------------------------------------------------------------ synthetic recipe
 
 def test_bf16_rounding_is_nearest_even():
