@@ -233,14 +233,16 @@ class Model:
             c.max_batch, c.n_kv_heads, self.seq_stride, c.head_dim)
 
     def cache_v(self, layer: int) -> torch.Tensor:
-        """V cache of one layer as [max_batch, G, seq_stride, d] (stored transposed)."""
+        """V cache of one layer as [max_batch, G, seq_stride, d] (a view of the stored
+        layout, which is transposed within blocks of 64 positions: [b][g][pos/64][d][64])."""
         c = self.cfg
         n = c.max_batch * c.n_kv_heads * self.seq_stride * c.head_dim
         es = 2 if self.spec.dtype == "bf16" else 4
         base = (layer * 2 + 1) * n * es
         vt = self.kv[base:base + n * es].view(self._elem()).view(
-            c.max_batch, c.n_kv_heads, c.head_dim, self.seq_stride)
-        return vt.transpose(2, 3)
+            c.max_batch, c.n_kv_heads, self.seq_stride // 64, c.head_dim, 64)
+        return vt.permute(0, 1, 2, 4, 3).reshape(c.max_batch, c.n_kv_heads, self.seq_stride,
+                                                 c.head_dim)
 
     def free(self):
         if getattr(self, "handle", None):

@@ -1,8 +1,8 @@
 // Causal grouped-query attention over the KV cache (article, sections 查询和键相乘, 掩码,
 // 注意力向量, 多头注意力): for query head h of the token at position p,
 //   o = sum_{n <= p} softmax_n(q . k_n / sqrt(d)) v_n,  k and v of KV head h / (H/G).
-// Cache layout: K [b][g][pos][d] (seq_stride positions per (b, g)), V transposed
-// [b][g][d][pos].
+// Cache layout: K [b][g][pos][d] (seq_stride positions per (b, g)); V transposed in
+// blocks of 64 positions, [b][g][pos/64][d][64] (vt_offset in epilogue.hpp).
 #include "launch.hpp"
 
 namespace lk {
@@ -58,7 +58,9 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int dd = lane + 64 * i;
-                if (dd < d) o[i] = fmaf(pj, to_f32(vb[(size_t)dd * seq_stride + c0 + jj]), o[i]);
+                if (dd < d)
+                    o[i] = fmaf(pj, to_f32(vb[((size_t)((c0 + jj) / VT_BLOCK) * d + dd) * VT_BLOCK +
+                                                 (c0 + jj) % VT_BLOCK]), o[i]);
             }
         }
     }
@@ -100,6 +102,7 @@ hipError_t launch_generic(const AttnArgs& a, hipStream_t s) {
 // get a score of -inf (article, section 多头注意力: the upper-triangular -inf mask).
 // ------------------------------------------------------------------------------------
 constexpr int FA_D = 128, FA_BKV = 64, FA_ROWS = 128;
+static_assert(FA_BKV == VT_BLOCK, "a key block is one V^T block");
 constexpr int FA_KCH = FA_BKV * FA_D / 8;       // 16-byte chunks of a K tile (1024)
 constexpr int FA_VCH = FA_D * FA_BKV / 4;       // 8-byte chunks of a V^T tile (2048)
 constexpr size_t FA_STAGE_BYTES = FA_KCH * 16 + FA_VCH * 8;  // 32 KB
@@ -167,7 +170,9 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
                           : u32x4{0, 0, 0, 0};
             const int vd = idx >> 3, vcn = idx & 7;
             const int key = kv0 + vcn * 8;
-            u32x4 v = (key < ctx) ? *reinterpret_cast<const u32x4*>(vbase + (size_t)vd * seq_stride + key)
+            // kv0 is a multiple of the 64-position V^T block: key % 64 = 8 vcn
+            u32x4 v = (key < ctx) ? *reinterpret_cast<const u32x4*>(
+                                        vbase + ((size_t)kb * FA_D + vd) * VT_BLOCK + vcn * 8)
                                   : u32x4{0, 0, 0, 0};
             vreg[i] = mask_keys8(v, key, ctx);
         }
@@ -362,13 +367,16 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
             for (int jj = 0; jj < 4; ++jj)
                 kr[t][jj] = (key < c1) ? *reinterpret_cast<const u32x4*>(src + 8 * jj) : u32x4{0, 0, 0, 0};
         }
+        // kb is a multiple of the 64-position V^T block
+        const bf16* vblk = vbase + (size_t)(kb / VT_BLOCK) * FA_D * VT_BLOCK;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            const bf16* row = vbase + (size_t)(16 * dt + col) * seq_stride;
+            const bf16* row = vblk + (size_t)(16 * dt + col) * VT_BLOCK;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int key = kb + 32 * j + 8 * kq;
-                const u32x4 v = (key < c1) ? *reinterpret_cast<const u32x4*>(row + key) : u32x4{0, 0, 0, 0};
+                const u32x4 v = (key < c1) ? *reinterpret_cast<const u32x4*>(row + 32 * j + 8 * kq)
+                                           : u32x4{0, 0, 0, 0};
                 vr[dt][j] = mask_keys8(v, key, c1);
             }
         }

@@ -4,6 +4,17 @@
 #pragma once
 #include "common.hpp"
 
+// The V cache holds V transposed inside blocks of VT_BLOCK positions: element (pos, i) of
+// sequence/head context c sits at [c][pos / VT_BLOCK][i][pos % VT_BLOCK].  A block of keys
+// is then one contiguous d x VT_BLOCK run, and the P.V operand (keys contiguous for a fixed
+// i) is a plain 16-byte load.
+constexpr int VT_BLOCK = 64;
+__host__ __device__ __forceinline__ size_t vt_offset(size_t ctx_index, int pos, int i, int d,
+                                                     int seq_stride) {
+    return ctx_index * (size_t)d * seq_stride + ((size_t)(pos / VT_BLOCK) * d + i) * VT_BLOCK +
+           (pos % VT_BLOCK);
+}
+
 // Weight rows of a GEMM, possibly split over up to three matrices stacked along n
 // (Q, K and V projections share one GEMM: rows [0,end0) of p0, then p1, then p2).
 template <typename T>
@@ -55,7 +66,8 @@ struct EpiSwiGLU {
 // attention kernel, k and v written to the KV cache at their positions.
 //   q   : [M][Nq] with Nq = H*d, row m = token (sequence m / S, position start + m % S)
 //   kc  : this layer's K cache [max_batch][G][seq_stride][d]
-//   vc  : this layer's V cache, transposed: [max_batch][G][d][seq_stride]
+//   vc  : this layer's V cache, transposed within blocks of 64 positions:
+//         [max_batch][G][seq_stride/64][d][64] (see VT_BLOCK)
 //   rope: [max_seq][d/2] of (cos, sin)
 template <typename T>
 struct EpiQKV {
@@ -84,9 +96,9 @@ struct EpiQKV {
             store4(kc + (((size_t)b * G + g) * seq_stride + pos) * d + j, v);
         } else {
             const int nv = n - Nq - Nk, g = nv / d, j = nv - g * d;
-            T* base = vc + (((size_t)b * G + g) * d + j) * seq_stride + pos;
+            T* base = vc + vt_offset((size_t)b * G + g, pos, j, d, seq_stride);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) base[(size_t)i * seq_stride] = from_f32<T>(v[i]);
+            for (int i = 0; i < 4; ++i) base[(size_t)i * VT_BLOCK] = from_f32<T>(v[i]);
         }
     }
 };
