@@ -49,11 +49,13 @@ Layout layout_of(const llama_config& c) {
     auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
     L.flags = take(256);
     L.rope = take((size_t)c.max_seq * (c.head_dim / 2) * sizeof(float2));
+    // GEMM inputs: the packed activation layout of the few-row GEMMs pads to 64 rows
+    const size_t arows = std::max<size_t>(rows, 64);
     L.x = take(rows * D * 4);
-    L.h = take(rows * D * es);
+    L.h = take(arows * D * es);
     L.q = take(rows * HD * es);
-    L.attn = take(rows * HD * es);
-    L.g = take(rows * (size_t)c.ffn_hidden * es);
+    L.attn = take(arows * HD * es);
+    L.g = take(arows * (size_t)c.ffn_hidden * es);
     L.logits = take((size_t)c.max_batch * c.vocab_size * 4);
     L.partials = take((size_t)c.max_batch * c.n_heads * splits * (c.head_dim + 2) * 4);
     L.tokbuf = take((size_t)c.max_batch * 4);
@@ -173,9 +175,12 @@ struct ProfScope {
     }
 };
 
-lk::GemmArgs<void> gemm_args(llama_model*, const void* A, int lda, const void* w, int M, int N, int K) {
+// A is in the activation layout act_pack(M, N, K) selects (written so by its producer).
+lk::GemmArgs<void> gemm_args(llama_model* m, const void* A, int lda, const void* w, int M, int N,
+                             int K) {
     lk::GemmArgs<void> g{};
     g.A = A; g.lda = lda;
+    g.a_pack = lk::act_pack(m->dt, M, N, K);
     g.W = WeightRows<void>{w, w, w, N, N, K};
     g.W3 = g.W;
     g.M = M; g.N = N; g.K = K;
@@ -190,10 +195,15 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
     const llama_layer_weights& w = m->layers[l];
     const int T = B * S, D = c.dim, H = c.n_heads, G = c.n_kv_heads, d = c.head_dim;
     const int Nq = H * d, Nk = G * d;
+    // each GEMM input is written in the layout its GEMM reads
+    const int pk_qkv = lk::act_pack(m->dt, T, Nq + 2 * Nk, D);
+    const int pk_wo = lk::act_pack(m->dt, T, D, Nq);
+    const int pk_up = lk::act_pack(m->dt, T, c.ffn_hidden, D);
+    const int pk_down = lk::act_pack(m->dt, T, D, c.ffn_hidden);
 
     {
         ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
-        HIP_TRY(lk::rmsnorm(m->dt, xin, 1, 0, w.attention_norm, m->h(), T, D, c.norm_eps, s));
+        HIP_TRY(lk::rmsnorm(m->dt, xin, 1, 0, w.attention_norm, m->h(), pk_qkv, T, D, c.norm_eps, s));
     }
 
     lk::GemmArgs<void> qkv = gemm_args(m, m->h(), D, w.wq, T, Nq + 2 * Nk, D);
@@ -205,7 +215,7 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
         HIP_TRY(lk::gemm_qkv(m->dt, qkv, eq, s));
     }
 
-    lk::AttnArgs aa{m->q(), m->kc(l), m->vc(l), m->attn(), B, S, start_pos, H, G, d,
+    lk::AttnArgs aa{m->q(), m->kc(l), m->vc(l), m->attn(), pk_wo, B, S, start_pos, H, G, d,
                     m->seq_stride, pos_dev, m->partials(), max_ctx};
     {
         ProfScope ps(m, LLAMA_KERNEL_ATTENTION, s);
@@ -219,13 +229,13 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
     }
     {
         ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
-        HIP_TRY(lk::rmsnorm(m->dt, xout, 1, 0, w.ffn_norm, m->h(), T, D, c.norm_eps, s));
+        HIP_TRY(lk::rmsnorm(m->dt, xout, 1, 0, w.ffn_norm, m->h(), pk_up, T, D, c.norm_eps, s));
     }
     lk::GemmArgs<void> ff = gemm_args(m, m->h(), D, w.w1, T, c.ffn_hidden, D);
     ff.W3 = WeightRows<void>{w.w3, w.w3, w.w3, c.ffn_hidden, c.ffn_hidden, D};
     {
         ProfScope ps(m, LLAMA_KERNEL_FFN_UP, s);
-        HIP_TRY(lk::gemm_swiglu(m->dt, ff, m->g(), c.ffn_hidden, s));
+        HIP_TRY(lk::gemm_swiglu(m->dt, ff, m->g(), c.ffn_hidden, pk_down, s));
     }
     {
         ProfScope ps(m, LLAMA_KERNEL_FFN_DOWN, s);
@@ -241,7 +251,9 @@ llama_status run_head(llama_model* m, int rows, int step, int offset, float* log
     const llama_config& c = m->cfg;
     {
         ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
-        HIP_TRY(lk::rmsnorm(m->dt, m->x(), step, offset, m->norm, m->h(), rows, c.dim, c.norm_eps, s));
+        HIP_TRY(lk::rmsnorm(m->dt, m->x(), step, offset, m->norm, m->h(),
+                            lk::act_pack(m->dt, rows, c.vocab_size, c.dim), rows, c.dim,
+                            c.norm_eps, s));
     }
     {
         ProfScope ps(m, LLAMA_KERNEL_LM_HEAD, s);

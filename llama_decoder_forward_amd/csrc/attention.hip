@@ -18,7 +18,7 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ 
                                                            T* __restrict__ out, int S,
                                                            int start_pos, const int* pos_dev,
                                                            int H, int G, int d, int seq_stride,
-                                                           float scale_log2) {
+                                                           float scale_log2, int out_pack) {
     const int row = blockIdx.x;  // b * S + s
     const int h = blockIdx.y;
     const int lane = threadIdx.x;
@@ -64,12 +64,11 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ 
             }
         }
     }
-    T* orow = out + (size_t)row * H * d + (size_t)h * d;
     const float inv = 1.0f / lrun;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int dd = lane + 64 * i;
-        if (dd < d) orow[dd] = from_f32<T>(o[i] * inv);
+        if (dd < d) out[act_offset(row, h * d + dd, H * d, out_pack)] = from_f32<T>(o[i] * inv);
     }
 }
 
@@ -81,7 +80,7 @@ hipError_t launch_generic(const AttnArgs& a, hipStream_t s) {
     dim3 grid(rows, a.H);
     attn_generic_kernel<T><<<grid, 64, 0, s>>>((const T*)a.q, (const T*)a.kc, (const T*)a.vc,
                                                (T*)a.out, a.S, a.start_pos, a.pos_dev, a.H, a.G,
-                                               a.d, a.seq_stride, scale_log2);
+                                               a.d, a.seq_stride, scale_log2, a.out_pack);
     return hipGetLastError();
 }
 
@@ -124,7 +123,7 @@ __device__ __forceinline__ u32x4 mask_keys8(u32x4 v, int first_key, int limit) {
 __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     bf16* __restrict__ out, int S, int start_pos, int H, int G, int seq_stride,
-    float scale_log2, int nqb) {
+    float scale_log2, int nqb, int out_pack) {
     extern __shared__ u32x4 fa_smem[];
     const int group = H / G, BQ = FA_ROWS / group;
     const int GB = gridDim.x / nqb;
@@ -278,14 +277,15 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
 
     if (!qvalid) return;
     const float inv = 1.0f / l_run;
-    bf16* orow = out + ((size_t)(b * S + sq) * H + hq) * FA_D;
 #pragma unroll
     for (int td = 0; td < 4; ++td)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
             float v[4] = {oacc[td][4 * gg] * inv, oacc[td][4 * gg + 1] * inv,
                           oacc[td][4 * gg + 2] * inv, oacc[td][4 * gg + 3] * inv};
-            store4(orow + 32 * td + 8 * gg + 4 * lh, v);
+            store4(out + act_offset(b * S + sq, hq * FA_D + 32 * td + 8 * gg + 4 * lh, H * FA_D,
+                                    out_pack),
+                   v);
         }
 }
 
@@ -303,7 +303,7 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
     }
     attn_prefill_mfma_kernel<<<nqb * a.G * a.B, 256, 2 * FA_STAGE_BYTES, s>>>(
         (const bf16*)a.q, (const bf16*)a.kc, (const bf16*)a.vc, (bf16*)a.out, a.S, a.start_pos,
-        a.H, a.G, a.seq_stride, scale_log2, nqb);
+        a.H, a.G, a.seq_stride, scale_log2, nqb, a.out_pack);
     return hipGetLastError();
 }
 
@@ -462,7 +462,8 @@ template <typename T>
 __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const float* __restrict__ part,
                                                                 T* __restrict__ out, int start_pos,
                                                                 const int* pos_dev, int H,
-                                                                int d, int max_splits, int chunk) {
+                                                                int d, int max_splits, int chunk,
+                                                                int out_pack) {
     __shared__ float wts[128];
     __shared__ float red[2];
     const int h = blockIdx.x, b = blockIdx.y;
@@ -490,17 +491,20 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const float* __r
     for (int i = t; i < d; i += blockDim.x) {
         float num = 0.0f;
         for (int s = 0; s < nsplit; ++s) num += wts[s] * pp[(size_t)s * (d + 2) + 2 + i];
-        out[(size_t)b * H * d + (size_t)h * d + i] = from_f32<T>(num / den);
+        out[act_offset(b, h * d + i, H * d, out_pack)] = from_f32<T>(num / den);
     }
 }
 
 // keys per split: enough workgroups (about 1024) to keep every CU streaming, at most 128
 // splits for the merge
+#ifndef LLAMA_DEC_TARGET_WGS
+#define LLAMA_DEC_TARGET_WGS 8192
+#endif
 int decode_chunk(const AttnArgs& a) {
     int chunk = 4 * DEC_BLOCK;
     while (chunk < 16 * 4 * DEC_BLOCK) {
         const long long splits = (a.max_ctx + chunk - 1) / chunk;
-        if (splits * a.G * a.B <= 2048 && splits <= 128) break;
+        if (splits * a.G * a.B <= LLAMA_DEC_TARGET_WGS && splits <= 128) break;
         chunk *= 2;
     }
     while ((a.max_ctx + chunk - 1) / chunk > 128) chunk *= 2;
@@ -518,7 +522,7 @@ hipError_t launch_decode_mfma(const AttnArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     attn_decode_merge_kernel<bf16><<<dim3(a.H, a.B), 128, 0, s>>>(
-        a.partials, (bf16*)a.out, a.start_pos, a.pos_dev, a.H, FA_D, max_splits, chunk);
+        a.partials, (bf16*)a.out, a.start_pos, a.pos_dev, a.H, FA_D, max_splits, chunk, a.out_pack);
     return hipGetLastError();
 }
 

@@ -56,7 +56,8 @@ hipError_t embed(Dt dt, const int* tokens, const void* E, float* x, int rows, in
 // row lives in registers between the two passes.  D % 8 == 0, D <= 256*8*MAXV.
 template <typename T, int MAXV>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int in_step, int in_off,
-                                                      const T* w, T* y, int D, float eps) {
+                                                      const T* w, T* y, int y_pack, int D,
+                                                      float eps) {
     const int r = blockIdx.x;
     const float* xr = x + ((size_t)r * in_step + in_off) * D;
     float v[MAXV][8];
@@ -79,7 +80,6 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int in_ste
     __syncthreads();
     const float total = red[0] + red[1] + red[2] + red[3];
     const float inv = 1.0f / sqrtf(total / (float)D + eps);
-    T* yr = y + (size_t)r * D;
 #pragma unroll
     for (int c = 0; c < MAXV; ++c) {
         const int i = (threadIdx.x + c * 256) * 8;
@@ -89,32 +89,35 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int in_ste
             float o[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) o[j] = (v[c][j] * inv) * wv[j];
-            store4(yr + i, o);
-            store4(yr + i + 4, o + 4);
+            T* yr = y + act_offset(r, i, D, y_pack);  // 8 consecutive values stay contiguous
+            store4(yr, o);
+            store4(yr + 4, o + 4);
         }
     }
 }
 
 template <typename T>
-static hipError_t rmsnorm_t(const float* x, int step, int off, const T* w, T* y, int rows, int D,
-                            float eps, hipStream_t s) {
+static hipError_t rmsnorm_t(const float* x, int step, int off, const T* w, T* y, int y_pack,
+                            int rows, int D, float eps, hipStream_t s) {
     if (D <= 2048)
-        rmsnorm_kernel<T, 1><<<rows, 256, 0, s>>>(x, step, off, w, y, D, eps);
+        rmsnorm_kernel<T, 1><<<rows, 256, 0, s>>>(x, step, off, w, y, y_pack, D, eps);
     else if (D <= 4096)
-        rmsnorm_kernel<T, 2><<<rows, 256, 0, s>>>(x, step, off, w, y, D, eps);
+        rmsnorm_kernel<T, 2><<<rows, 256, 0, s>>>(x, step, off, w, y, y_pack, D, eps);
     else if (D <= 8192)
-        rmsnorm_kernel<T, 4><<<rows, 256, 0, s>>>(x, step, off, w, y, D, eps);
+        rmsnorm_kernel<T, 4><<<rows, 256, 0, s>>>(x, step, off, w, y, y_pack, D, eps);
     else
-        rmsnorm_kernel<T, 8><<<rows, 256, 0, s>>>(x, step, off, w, y, D, eps);
+        rmsnorm_kernel<T, 8><<<rows, 256, 0, s>>>(x, step, off, w, y, y_pack, D, eps);
     return hipGetLastError();
 }
 
 hipError_t rmsnorm(Dt dt, const float* x, int in_row_step, int in_row_offset, const void* w,
-                   void* y, int rows, int D, float eps, hipStream_t s) {
+                   void* y, int y_pack, int rows, int D, float eps, hipStream_t s) {
     if (rows == 0) return hipSuccess;
     if (dt == Dt::BF16)
-        return rmsnorm_t<bf16>(x, in_row_step, in_row_offset, (const bf16*)w, (bf16*)y, rows, D, eps, s);
-    return rmsnorm_t<float>(x, in_row_step, in_row_offset, (const float*)w, (float*)y, rows, D, eps, s);
+        return rmsnorm_t<bf16>(x, in_row_step, in_row_offset, (const bf16*)w, (bf16*)y, y_pack, rows,
+                               D, eps, s);
+    return rmsnorm_t<float>(x, in_row_step, in_row_offset, (const float*)w, (float*)y, y_pack, rows,
+                            D, eps, s);
 }
 
 // Greedy choice per row: the largest logit, lowest index among equals (article, section

@@ -15,6 +15,23 @@ __host__ __device__ __forceinline__ size_t vt_offset(size_t ctx_index, int pos, 
            (pos % VT_BLOCK);
 }
 
+// Activation layout of the few-row (decode) GEMMs.  pack == 0: plain row-major [m][ld].
+// pack = P > 0 (a power of two >= the row count, at most 64): the values are stored in the
+// order the weight-streaming GEMM feeds them to its 16x16x32 MFMAs, so that each of its
+// activation loads is one contiguous run.  Rows are grouped in blocks of R = min(P, 16); for
+// k-block kb = k / 128, slice j = (k / 32) % 4 and row block mb = m / R, the run holds the
+// 8 values k - k % 8 .. of row m at position (m % R) + R * ((k / 8) % 4).  With P < 16 the
+// GEMM's 16 operand lanes reread the R stored rows (their results are never stored), so a
+// batch of 4 moves 4 rows, not 16.  Any four consecutive k starting at a multiple of 4 stay
+// contiguous.  The producers of a GEMM's input (RMSNorm, attention output, SwiGLU) write
+// this layout when that GEMM runs on the weight-streaming path.
+__host__ __device__ __forceinline__ size_t act_offset(int m, int k, int ld, int pack) {
+    if (pack == 0) return (size_t)m * ld + k;
+    const int R = pack < 16 ? pack : 16;
+    const size_t blk = ((size_t)(k >> 7) * 4 + ((k >> 5) & 3)) * (pack / R) + m / R;
+    return ((blk * 4 + ((k >> 3) & 3)) * R + (m & (R - 1))) * 8 + (k & 7);
+}
+
 // Weight rows of a GEMM, possibly split over up to three matrices stacked along n
 // (Q, K and V projections share one GEMM: rows [0,end0) of p0, then p1, then p2).
 template <typename T>
@@ -50,14 +67,15 @@ struct EpiResidual {
 
 // SwiGLU gate (article, section 前馈神经网络层): g[m][n] = silu(h.w1_n) * (h.w3_n),
 // silu(z) = z / (1 + exp(-z)).
+// g is stored in the activation layout of the down projection (act_offset, pack).
 template <typename T>
 struct EpiSwiGLU {
-    T* g; int ld;
+    T* g; int ld; int pack;
     __device__ __forceinline__ void operator()(int m, int n, float gate[4], float up[4]) const {
         float o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = gate[i] / (1.0f + __expf(-gate[i])) * up[i];
-        store4(g + (size_t)m * ld + n, o);
+        store4(g + act_offset(m, n, ld, pack), o);
     }
 };
 

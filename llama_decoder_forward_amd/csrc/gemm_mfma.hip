@@ -219,7 +219,7 @@ hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
 template <bool DUAL, typename Epi>
 hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
-    if (skinny_ok(g)) return skinny_launch<DUAL>(g, e, s);
+    if (g.a_pack > 0) return skinny_launch<DUAL>(g, e, s);
     if (g.M <= 32) return launch_cfg<128, 32, 64, 3, 4, 1, DUAL>(g, e, s);
     if constexpr (DUAL) {
         return launch_cfg<128, 256, 64, 2, 2, 4, DUAL>(g, e, s);
@@ -240,9 +240,10 @@ hipError_t gemm_residual(Dt dt, const GemmArgs<void>& g, EpiResidual e, hipStrea
     if (dt == Dt::F32) return simt_residual(g, e, s);
     return launch<false>(g, e, s);
 }
-hipError_t gemm_swiglu(Dt dt, const GemmArgs<void>& g, void* out, int ld, hipStream_t s) {
+hipError_t gemm_swiglu(Dt dt, const GemmArgs<void>& g, void* out, int ld, int out_pack,
+                       hipStream_t s) {
     if (dt == Dt::F32) return simt_swiglu(g, out, ld, s);
-    return launch<true>(g, EpiSwiGLU<bf16>{(bf16*)out, ld}, s);
+    return launch<true>(g, EpiSwiGLU<bf16>{(bf16*)out, ld, out_pack}, s);
 }
 hipError_t gemm_qkv(Dt dt, const GemmArgs<void>& g, const EpiQKV<void>& e, hipStream_t s) {
     if (dt == Dt::F32) return simt_qkv(g, e, s);

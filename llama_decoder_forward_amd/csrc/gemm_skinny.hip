@@ -4,12 +4,16 @@
 // The cost is reading W once from HBM, so the kernel is shaped for bandwidth.  A workgroup
 // owns a strip of RT x 16 weight rows (and as many of W3 for the SwiGLU pair); its NW waves
 // split K between them and stream their share in 128-wide k blocks straight from global
-// memory into MFMA operands, two blocks in flight (no LDS staging: the activations are a few
-// hundred KB and stay in L2).  Lane (row n = l%16, quarter kq = l/16) reads 64 contiguous
-// bytes of its row per block; the activation operand uses the same k permutation.  The
-// waves' partial tiles are summed through LDS in wave order (deterministic), and the
-// result, lane (token m = l%16 + 16 mb, quarter kq) holding rows n = 4kq..4kq+3, goes to the
-// epilogue in the four-column groups it takes.
+// memory into MFMA operands, up to three blocks in flight (no LDS staging: the activations
+// are a few hundred KB and stay in L2).  For k-block kb and slice j (32 k),
+// lane (row n = l%16, quarter kq = l/16) reads the 8 weights k = 128 kb + 32 j + 8 kq ..;
+// the four lanes of a row cover 64 contiguous bytes.  The activations arrive in the packed
+// layout of act_offset, where the matching operand of every (kb, j, row block) is one
+// contiguous 1 KB run: a fully coalesced load, where the row-major layout would touch 16
+// rows per load (measured on MI355X: half the time at batch 32).  The waves' partial tiles
+// are summed through LDS in wave order (deterministic), and the result, lane (token
+// m = l%16 + 16 mb, quarter kq) holding rows n = 4kq..4kq+3, goes to the epilogue in the
+// four-column groups it takes.
 #include "launch.hpp"
 
 namespace lk {
@@ -21,7 +25,7 @@ constexpr int SK_KB = 128;   // k per block
 
 template <int NW, int RT, int MB, bool DUAL, typename Epi>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
-    const bf16* __restrict__ A, int lda, WeightRows<bf16> W, WeightRows<bf16> W3, int M, int N,
+    const bf16* __restrict__ A, int pack, WeightRows<bf16> W, WeightRows<bf16> W3, int M, int N,
     int K, Epi epi) {
     constexpr int NA = DUAL ? 2 : 1;
     __shared__ f32x4 red[NW > 1 ? NW - 1 : 1][NA * RT * MB][64];
@@ -34,17 +38,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     const bf16* w3row[DUAL ? RT : 1];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-        wrow[r] = W.row(n0 + 16 * r + col) + kq * 32;
-        if constexpr (DUAL) w3row[r] = W3.row(n0 + 16 * r + col) + kq * 32;
+        wrow[r] = W.row(n0 + 16 * r + col) + kq * 8;
+        if constexpr (DUAL) w3row[r] = W3.row(n0 + 16 * r + col) + kq * 8;
     }
-    const bf16* arow[MB];
-    bool avalid[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int m = mb * 16 + col;
-        avalid[mb] = m < M;
-        arow[mb] = A + (size_t)(avalid[mb] ? m : 0) * lda + kq * 32;
-    }
+    // packed activations (act_offset): run (kb, j, mb) is 32 R values; lane (col, kq) takes
+    // the 8 of row col % R
+    const int R = pack < 16 ? pack : 16;
+    const bf16* abase = A + (kq * R + (col & (R - 1))) * 8;
 
     f32x4 acc[RT][MB], acc3[DUAL ? RT : 1][MB];
 #pragma unroll
@@ -60,8 +60,11 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     const int kb0 = wave * per;
     const int kb1 = min(blocks, kb0 + per);
 
-    // two register stages when they fit, one otherwise (then other waves hide the latency)
-    constexpr int NS = (RT * NA + MB) <= 4 ? 2 : 1;
+    // register stages: as many blocks in flight as about 96 VGPRs hold (a block takes 16
+    // VGPRs per weight tile and per activation row block).  Deeper pipelines cost more in
+    // occupancy than they gain (measured on MI355X, batch 1 to 64).
+    constexpr int NS0 = 96 / ((RT * NA + MB) * 16);
+    constexpr int NS = NS0 < 1 ? 1 : NS0 > 4 ? 4 : NS0;
     u32x4 w[NS][RT][4], w3[NS][DUAL ? RT : 1][4], a[NS][MB][4];
     auto load = [&](int st, int kb) {
         const int k = kb * SK_KB;
@@ -69,15 +72,15 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
         for (int r = 0; r < RT; ++r)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                w[st][r][j] = *reinterpret_cast<const u32x4*>(wrow[r] + k + 8 * j);
-                if constexpr (DUAL) w3[st][r][j] = *reinterpret_cast<const u32x4*>(w3row[r] + k + 8 * j);
+                w[st][r][j] = *reinterpret_cast<const u32x4*>(wrow[r] + k + 32 * j);
+                if constexpr (DUAL) w3[st][r][j] = *reinterpret_cast<const u32x4*>(w3row[r] + k + 32 * j);
             }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                a[st][mb][j] = avalid[mb] ? *reinterpret_cast<const u32x4*>(arow[mb] + k + 8 * j)
-                                          : u32x4{0, 0, 0, 0};
+                a[st][mb][j] = *reinterpret_cast<const u32x4*>(
+                    abase + ((size_t)(kb * 4 + j) * MB + mb) * 32 * R);
     };
     auto compute = [&](int st) {
 #pragma unroll
@@ -93,21 +96,26 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
                             __builtin_bit_cast(bf16x8, w3[st][r][j]), __builtin_bit_cast(bf16x8, a[st][mb][j]), acc3[r][mb], 0, 0, 0);
                 }
     };
-    if constexpr (NS == 2) {
-        if (kb0 < kb1) load(0, kb0);
+    // Block kb0 + i lives in stage i % NS, NS - 1 blocks ahead are in flight.  The loads
+    // are unconditional (past the end they reread the last block, which the cache holds):
+    // a branch around a load makes the compiler wait for every outstanding load.
+    if (kb0 < kb1) {
+        const int last = kb1 - 1;
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i) load(i, min(kb0 + i, last));
         int kb = kb0;
-        for (; kb + 1 < kb1; kb += 2) {
-            load(1, kb + 1);
-            compute(0);
-            if (kb + 2 < kb1) load(0, kb + 2);
-            compute(1);
+        for (; kb + NS <= kb1; kb += NS) {
+#pragma unroll
+            for (int i = 0; i < NS; ++i) {
+                load((i + NS - 1) % NS, min(kb + i + NS - 1, last));
+                __builtin_amdgcn_sched_barrier(0);  // issue the loads before waiting on block i
+                compute(i);
+            }
         }
-        if (kb < kb1) compute(0);
-    } else {
-        for (int kb = kb0; kb < kb1; ++kb) {
-            load(0, kb);
-            compute(0);
-        }
+        // the last < NS blocks are already loaded
+#pragma unroll
+        for (int i = 0; i < NS - 1; ++i)
+            if (kb + i < kb1) compute(i);
     }
 
     if constexpr (NW > 1) {
@@ -122,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
         }
         __syncthreads();
         if (wave > 0) return;
-#pragma unroll
+#pragma unroll 1
         for (int w2 = 0; w2 < NW - 1; ++w2)
 #pragma unroll
             for (int r = 0; r < RT; ++r)
@@ -157,18 +165,21 @@ hipError_t launch_mb(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     const bf16* A = (const bf16*)g.A;
     // waves per strip: enough waves in flight to cover HBM latency (about 2-4k waves)
     if (strips >= 2048)
-        gemm_skinny_kernel<2, RT, MB, DUAL, Epi><<<strips, 128, 0, s>>>(A, g.lda, W, W3, g.M, g.N, g.K, e);
+        gemm_skinny_kernel<2, RT, MB, DUAL, Epi><<<strips, 128, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
     else if (strips >= 384)
-        gemm_skinny_kernel<4, RT, MB, DUAL, Epi><<<strips, 256, 0, s>>>(A, g.lda, W, W3, g.M, g.N, g.K, e);
+        gemm_skinny_kernel<4, RT, MB, DUAL, Epi><<<strips, 256, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
     else
-        gemm_skinny_kernel<8, RT, MB, DUAL, Epi><<<strips, 512, 0, s>>>(A, g.lda, W, W3, g.M, g.N, g.K, e);
+        gemm_skinny_kernel<8, RT, MB, DUAL, Epi><<<strips, 512, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool skinny_ok(const GemmArgs<void>& g) {
-    return g.M <= 64 && g.N % SK_ROWS == 0 && g.K % SK_KB == 0;
+int act_pack(Dt dt, int M, int N, int K) {
+    if (dt != Dt::BF16 || M < 1 || M > 64 || N % SK_ROWS != 0 || K % SK_KB != 0) return 0;
+    int P = 1;
+    while (P < M) P *= 2;
+    return P;
 }
 
 // Row tiles per wave (RT): every activation fragment serves RT weight tiles, which keeps the
@@ -177,15 +188,17 @@ bool skinny_ok(const GemmArgs<void>& g) {
 // vocabulary projection, the gate/up pair).  Measured on MI355X at batch 4 and 32.
 template <bool DUAL, typename Epi>
 hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
+    if (g.a_pack != act_pack(Dt::BF16, g.M, g.N, g.K)) return hipErrorInvalidValue;
+    const int mb = g.a_pack < 16 ? 1 : g.a_pack / 16;  // 16-row MFMA column blocks
     const bool wide = g.N >= 16384;
-    if (g.M <= 16) return launch_mb<1, 1, DUAL>(g, e, s);
+    if (mb == 1) return launch_mb<1, 1, DUAL>(g, e, s);
     if constexpr (DUAL) {
-        if (g.M <= 32 && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 2, DUAL>(g, e, s);
-        if (g.M <= 32) return launch_mb<1, 2, DUAL>(g, e, s);
+        if (mb == 2 && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 2, DUAL>(g, e, s);
+        if (mb == 2) return launch_mb<1, 2, DUAL>(g, e, s);
         return launch_mb<1, 4, DUAL>(g, e, s);
     } else {
-        if (g.M <= 32 && wide && g.N % (SK_ROWS * 4) == 0) return launch_mb<4, 2, DUAL>(g, e, s);
-        if (g.M <= 32) return launch_mb<1, 2, DUAL>(g, e, s);
+        if (mb == 2 && wide && g.N % (SK_ROWS * 4) == 0) return launch_mb<4, 2, DUAL>(g, e, s);
+        if (mb == 2) return launch_mb<1, 2, DUAL>(g, e, s);
         if (wide && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 4, DUAL>(g, e, s);
         return launch_mb<1, 4, DUAL>(g, e, s);
     }

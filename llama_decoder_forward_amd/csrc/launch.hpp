@@ -11,9 +11,10 @@ enum class Dt { BF16, F32 };
 hipError_t rope_table(float2* rope, int max_seq, int d, float theta, hipStream_t s);
 hipError_t embed(Dt dt, const int* tokens, const void* E, float* x, int rows, int D, int V,
                  uint32_t* err, hipStream_t s);
-// y[r] = rmsnorm(x[r * in_stride_rows + in_offset_rows]) for r < rows
+// y[r] = rmsnorm(x[r * in_stride_rows + in_offset_rows]) for r < rows, y in the activation
+// layout act_offset(r, i, D, y_pack)
 hipError_t rmsnorm(Dt dt, const float* x, int in_row_step, int in_row_offset, const void* w,
-                   void* y, int rows, int D, float eps, hipStream_t s);
+                   void* y, int y_pack, int rows, int D, float eps, hipStream_t s);
 size_t argmax_scratch_bytes(int rows, int V);
 hipError_t argmax(const float* logits, int rows, int V, int* out, int* out2, int out2_step,
                   const int* counter, void* scratch, uint32_t* err, hipStream_t s);
@@ -25,17 +26,20 @@ hipError_t set_counters(int* pos, int pos_value, int* step, hipStream_t s);
 // ---- GEMMs: acc[m][n] = sum_k A[m][k] W[n][k]  (gemm_mfma.hip, gemm_simt.hip, gemm_skinny.hip)
 template <typename T> struct GemmArgs {
     const T* A; int lda;
+    int a_pack;         // activation layout of A (act_offset); > 0 selects the weight-streaming path
     WeightRows<T> W;
     WeightRows<T> W3;  // second weight set of the SwiGLU gate/up GEMM
     int M, N, K;
 };
-// weight-streaming path for few rows (gemm_skinny.hip)
-bool skinny_ok(const GemmArgs<void>& g);
+// Weight-streaming path for few rows (gemm_skinny.hip).  act_pack returns the activation
+// layout (row blocks of 16) its input must be written in, or 0 where the GEMM of these sizes
+// takes the tiled or fp32 path and reads plain row-major A.
+int act_pack(Dt dt, int M, int N, int K);
 template <bool DUAL, typename Epi>
 hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s);
 hipError_t gemm_store_f32(Dt dt, const GemmArgs<void>& g, EpiStoreF32 e, hipStream_t s);
 hipError_t gemm_residual(Dt dt, const GemmArgs<void>& g, EpiResidual e, hipStream_t s);
-hipError_t gemm_swiglu(Dt dt, const GemmArgs<void>& g, void* out, int ld, hipStream_t s);
+hipError_t gemm_swiglu(Dt dt, const GemmArgs<void>& g, void* out, int ld, int out_pack, hipStream_t s);
 hipError_t gemm_qkv(Dt dt, const GemmArgs<void>& g, const EpiQKV<void>& e, hipStream_t s);
 
 // ---- attention (attention.hip)
@@ -43,7 +47,8 @@ struct AttnArgs {
     const void* q;   // [rows][H*d], row = b*S + s
     const void* kc;  // layer K cache
     const void* vc;  // layer V^T cache
-    void* out;       // [rows][H*d]
+    void* out;       // [rows][H*d] in the activation layout act_offset(row, col, H*d, out_pack)
+    int out_pack;
     int B, S, start_pos, H, G, d, seq_stride;
     const int* pos_dev;
     float* partials; // decode split-K scratch
