@@ -116,11 +116,24 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
     for (int st = 0; st < STAGES - 1; ++st)
         if (st < nk) issue(st, st * BK);
 
+    // The copies of tile kt + STAGES - 1 are spread over the k-steps of tile kt, a few
+    // behind each step's MFMAs: issued all at once, the 8 waves' copies queue up in the
+    // address unit and every wave stalls behind its own before reaching its MFMAs.
+    constexpr int KSTEPS = BK / 16;
+    constexpr int PPS = (SPW + KSTEPS - 1) / KSTEPS;  // copies per k-step
+    auto issue_part = [&](int st, int k0, int kk) {
+#pragma unroll
+        for (int q = 0; q < PPS; ++q) {
+            const int i = kk * PPS + q;
+            if (i < SPW) lds_dma16(src[i] + k0, lds0 + st * STAGE + (wave + i * NW) * 1024);
+        }
+    };
     for (int kt = 0; kt < nk; ++kt) {
         // tile kt has landed once at most the copies of the later tiles are outstanding
         if (kt + STAGES - 2 < nk) wait_vm_and_barrier<(STAGES - 2) * SPW>();
         else wait_vm_and_barrier<0>();
-        if (kt + STAGES - 1 < nk) issue((kt + STAGES - 1) % STAGES, (kt + STAGES - 1) * BK);
+        const bool more = kt + STAGES - 1 < nk;
+        const int nst = (kt + STAGES - 1) % STAGES, nk0 = (kt + STAGES - 1) * BK;
         const char* base = reinterpret_cast<const char*>(lds) + (kt % STAGES) * STAGE;
         // fragments of k-step kk+1 are read from LDS while the MFMAs of step kk run
         bf16x8 fa[2][TN], fa3[2][DUAL ? TN : 1], fb[2][TM];
@@ -161,6 +174,11 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
+            }
+            if (more) {
+                __builtin_amdgcn_sched_barrier(0);
+                issue_part(nst, nk0, kk);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
@@ -210,12 +228,15 @@ hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Tile shapes per GEMM shape, measured on MI355X (8B-shaped layer at 2048 and 32768 tokens):
+// Tile shapes per GEMM shape, measured on MI355X (8B-shaped layer at 2048 tokens):
 //  - wide weight matrices (Q/K/V, the vocabulary) and every GEMM with many token tiles:
-//    256 x 256 macro tile, 8 waves of 128 x 64, two 64-deep LDS stages;
+//    256 tokens x 256 or 192 weight rows, 8 waves, two 64-deep LDS stages.  192 rows is
+//    taken when it covers the 256 CUs in fewer rounds of tiles for the same work (Q/K/V at
+//    2048 tokens: 256 tiles instead of 192, 117 us instead of 150);
 //  - the SwiGLU gate/up pair: 128 rows of W1 + 128 of W3 against 256 tokens, 8 waves;
-//  - N = dim outputs (WO, W2) at a few thousand tokens: 128 x 128, 4 waves, so that the
-//    grid still covers the 256 CUs.
+//  - N = dim outputs (WO, W2) at a few thousand tokens: 256 weight rows x 128 tokens, 4 waves
+//    of 128 x 64, three LDS stages (256 tiles at 2048 tokens; the per-tile operand traffic
+//    of 128 x 128 tiles left those GEMMs bound by the global-to-LDS copies).
 template <bool DUAL, typename Epi>
 hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
@@ -224,9 +245,16 @@ hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     if constexpr (DUAL) {
         return launch_cfg<128, 256, 64, 2, 2, 4, DUAL>(g, e, s);
     } else {
-        const long long tiles256 = (long long)((g.N + 255) / 256) * ((g.M + 255) / 256);
-        if (g.N >= 6144 || tiles256 >= 512) return launch_cfg<256, 256, 64, 2, 2, 4, DUAL>(g, e, s);
-        return launch_cfg<128, 128, 64, 2, 2, 2, DUAL>(g, e, s);
+        const long long mt = (g.M + 255) / 256;
+        const long long t256 = (long long)((g.N + 255) / 256) * mt;
+        if (g.N >= 6144 || t256 >= 512) {
+            // rounds of 256 tiles x rows per tile: the smaller wins, ties go to 256 rows
+            const long long t192 = (long long)((g.N + 191) / 192) * mt;
+            if (((t192 + 255) / 256) * 192 < ((t256 + 255) / 256) * 256)
+                return launch_cfg<192, 256, 64, 2, 2, 4, DUAL>(g, e, s);
+            return launch_cfg<256, 256, 64, 2, 2, 4, DUAL>(g, e, s);
+        }
+        return launch_cfg<256, 128, 64, 3, 2, 2, DUAL>(g, e, s);
     }
 }
 
