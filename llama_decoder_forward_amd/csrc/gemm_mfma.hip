@@ -38,13 +38,14 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-// Block tile BN weight rows x BM tokens x BK, STAGES-deep LDS ring.  LDS row = BK bf16
+// Block tile BN weight rows x BM tokens x BK, STAGES-deep LDS ring; the grid covers weight
+// rows [n_begin, N) and all M tokens.  LDS row = BK bf16
 // (RB bytes) split in 16-byte chunks; chunk c of row r is stored at c ^ swz(r) so that the
 // MFMA operand reads of consecutive rows hit distinct banks.
 template <int BN, int BM, int BK, int STAGES, int WN, int WM, bool DUAL, typename Epi>
 __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
     const bf16* __restrict__ A, int lda, WeightRows<bf16> W, WeightRows<bf16> W3, int M, int N,
-    int K, Epi epi) {
+    int K, int n_begin, Epi epi) {
     constexpr int NW = WN * WM;
     constexpr int NA = DUAL ? 2 : 1;
     constexpr int ROWS = NA * BN + BM;
@@ -65,14 +66,14 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
 
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wn = wave / WM, wm = wave % WM;
-    const int nt_m = (M + BM - 1) / BM, nt_n = (N + BN - 1) / BN;
+    const int nt_m = (M + BM - 1) / BM, nt_n = (N - n_begin + BN - 1) / BN;
     const int tiles = nt_m * nt_n;
     int bid = blockIdx.x;
     // workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous run of
     // tiles (token tiles fastest) so that tiles sharing weight rows share that XCD's L2
     if (tiles % 8 == 0) bid = (bid & 7) * (tiles >> 3) + (bid >> 3);
     const int tile_m = bid % nt_m, tile_n = bid / nt_m;
-    const int n0 = tile_n * BN, m0 = tile_m * BM;
+    const int n0 = n_begin + tile_n * BN, m0 = tile_m * BM;
 
     // this lane's source address for each of its wave's copies of a stage
     const bf16* src[SPW];
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
 }
 
 template <int BN, int BM, int BK, int STAGES, int WN, int WM, bool DUAL, typename Epi>
-hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
+hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s, int n_begin = 0) {
     const WeightRows<bf16> W{(const bf16*)g.W.p0, (const bf16*)g.W.p1, (const bf16*)g.W.p2, g.W.end0, g.W.end1, g.W.ld};
     const WeightRows<bf16> W3{(const bf16*)g.W3.p0, (const bf16*)g.W3.p1, (const bf16*)g.W3.p2, g.W3.end0, g.W3.end1, g.W3.ld};
     constexpr int ROWS = (DUAL ? 2 : 1) * BN + BM;
@@ -223,8 +224,9 @@ hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
         if (err != hipSuccess) return err;
         attr_set = true;
     }
-    const int tiles = ((g.N + BN - 1) / BN) * ((g.M + BM - 1) / BM);
-    kern<<<tiles, WN * WM * 64, lds_bytes, s>>>((const bf16*)g.A, g.lda, W, W3, g.M, g.N, g.K, e);
+    const int tiles = ((g.N - n_begin + BN - 1) / BN) * ((g.M + BM - 1) / BM);
+    kern<<<tiles, WN * WM * 64, lds_bytes, s>>>((const bf16*)g.A, g.lda, W, W3, g.M, g.N, g.K,
+                                                n_begin, e);
     return hipGetLastError();
 }
 
@@ -233,7 +235,11 @@ hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
 //    256 tokens x 256 or 192 weight rows, 8 waves, two 64-deep LDS stages.  192 rows is
 //    taken when it covers the 256 CUs in fewer rounds of tiles for the same work (Q/K/V at
 //    2048 tokens: 256 tiles instead of 192, 117 us instead of 150);
-//  - the SwiGLU gate/up pair: 128 rows of W1 + 128 of W3 against 256 tokens, 8 waves;
+//  - the SwiGLU gate/up pair: 128 rows of W1 + 128 of W3 against 256 tokens, 8 waves.  When
+//    the tiles fill the CUs a few times over plus a final round less than half full (2048
+//    tokens: 896 tiles = 3.5 rounds), the weight rows of that last round go to a second
+//    launch of half-height tiles (128 tokens) that fills one round: the last round then
+//    takes about half a tile's time instead of a whole one;
 //  - N = dim outputs (WO, W2) at a few thousand tokens: 256 weight rows x 128 tokens, 4 waves
 //    of 128 x 64, three LDS stages (256 tiles at 2048 tokens; the per-tile operand traffic
 //    of 128 x 128 tiles left those GEMMs bound by the global-to-LDS copies).
@@ -243,6 +249,16 @@ hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     if (g.a_pack > 0) return skinny_launch<DUAL>(g, e, s);
     if (g.M <= 32) return launch_cfg<128, 32, 64, 3, 4, 1, DUAL>(g, e, s);
     if constexpr (DUAL) {
+        const int strips = (g.N + 127) / 128, mt = (g.M + 255) / 256;
+        const long long tiles = (long long)strips * mt, rest = tiles % 256;
+        if (tiles > 256 && tiles <= 8 * 256 && rest > 0 && rest <= 128 && rest % mt == 0) {
+            const int n_tail = (int)(strips - rest / mt) * 128;  // rows of the last round
+            GemmArgs<void> head = g;
+            head.N = n_tail;
+            hipError_t err = launch_cfg<128, 256, 64, 2, 2, 4, DUAL>(head, e, s);
+            if (err != hipSuccess) return err;
+            return launch_cfg<128, 128, 64, 3, 2, 2, DUAL>(g, e, s, n_tail);
+        }
         return launch_cfg<128, 256, 64, 2, 2, 4, DUAL>(g, e, s);
     } else {
         const long long mt = (g.M + 255) / 256;
