@@ -108,7 +108,9 @@ size_t llama_workspace_bytes(const llama_config *cfg);
 /* Validate cfg, borrow the weights, KV cache and workspace, and return a handle in *out.
  * Makes no device call; the RoPE table (cos and sin of m*theta_i for every position m <
  * max_seq, angles formed in double precision, article section 位置编码) is built on the
- * device by the first call that needs it.  kv_bytes and ws_bytes must be at least the
+ * device by the first call that needs it, which also zero-fills the KV cache (attention
+ * reads whole 64-position blocks and weights positions past the context by exactly 0, so
+ * every cached value must be finite).  kv_bytes and ws_bytes must be at least the
  * sizes above, and both buffers 256-byte aligned.  Errors: INVALID_ARG (null pointers),
  * SHAPE (dim != n_heads*head_dim, H % G != 0, odd or >256 head_dim, non-positive sizes,
  * bf16 dims that are not multiples of 64), DTYPE, CAPACITY (buffers too small), ALLOC. */

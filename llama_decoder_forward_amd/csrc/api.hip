@@ -141,10 +141,15 @@ namespace {
         if (e_ != hipSuccess) return fail(LLAMA_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
     } while (0)
 
+// First-use set-up on the caller's stream: device flags, the rotary table, and a zero fill
+// of the KV cache.  Attention reads whole 64-position blocks of the cache and gives the
+// positions past a sequence's context probability 0; with every cached value finite (zero
+// or written by a layer) those positions add exactly 0 * V.
 llama_status ensure_rope(llama_model* m, hipStream_t s) {
     if (m->rope_ready) return LLAMA_OK;
     HIP_TRY(lk::zero_u32(m->deverr(), 64, s));  // device flags and counters (first 256 bytes)
     HIP_TRY(lk::rope_table(m->rope(), m->cfg.max_seq, m->cfg.head_dim, m->cfg.rope_theta, s));
+    HIP_TRY(lk::zero_bytes(m->kv, llama_kv_cache_bytes(&m->cfg), s));
     m->rope_ready = true;
     return LLAMA_OK;
 }

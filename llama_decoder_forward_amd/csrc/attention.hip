@@ -102,9 +102,8 @@ hipError_t launch_generic(const AttnArgs& a, hipStream_t s) {
 // ------------------------------------------------------------------------------------
 constexpr int FA_D = 128, FA_BKV = 64, FA_ROWS = 128;
 static_assert(FA_BKV == VT_BLOCK, "a key block is one V^T block");
-constexpr int FA_KCH = FA_BKV * FA_D / 8;       // 16-byte chunks of a K tile (1024)
-constexpr int FA_VCH = FA_D * FA_BKV / 4;       // 8-byte chunks of a V^T tile (2048)
-constexpr size_t FA_STAGE_BYTES = FA_KCH * 16 + FA_VCH * 8;  // 32 KB
+constexpr int FA_KBYTES = FA_BKV * FA_D * 2;   // K tile: 64 keys x 256 B
+constexpr int FA_STAGE_BYTES = 2 * FA_KBYTES;  // + V^T tile: 128 d x 128 B
 
 __device__ __forceinline__ u32x4 mask_keys8(u32x4 v, int first_key, int limit) {
     // zero the bf16 elements whose key index (first_key + e) is >= limit
@@ -120,171 +119,206 @@ __device__ __forceinline__ u32x4 mask_keys8(u32x4 v, int first_key, int limit) {
     return v;
 }
 
-__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
+// One 32-row query tile of a wave: Q fragments (B operand of S^T = K Q^T, lane lr holds
+// query row lr, d = 8 (2 kk + lh) ..), the O^T accumulator and the online-softmax state of
+// the lane's query column.
+struct FaTile {
+    bf16x8 qf[8];
+    f32x16 o[4];
+    float m, l;
+    int hq, sq, qpos, p_lo, nkb;
+    bool valid;
+};
+
+__device__ __forceinline__ void fa_tile_init(FaTile& T, const bf16* __restrict__ q, int blk, int r,
+                                             int b, int g, int S, int start_pos, int H,
+                                             int group, int BQ, int lh) {
+    T.hq = g * group + r / BQ;
+    T.sq = blk * BQ + r % BQ;
+    T.valid = T.sq < S;
+    T.qpos = start_pos + T.sq;
+    T.p_lo = start_pos + blk * BQ;
+    const int p_hi = start_pos + min(S, blk * BQ + BQ) - 1;
+    T.nkb = (p_hi + 1 + FA_BKV - 1) / FA_BKV;   // keys this tile's block needs: 0..p_hi
+    const bf16* qrow = q + ((size_t)(b * S + (T.valid ? T.sq : 0)) * H + T.hq) * FA_D;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+        T.qf[kk] = T.valid ? *reinterpret_cast<const bf16x8*>(qrow + (kk * 2 + lh) * 8) : bf16x8{};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) T.o[i] = f32x16{};
+    T.m = -INFINITY;
+    T.l = 0.0f;
+}
+
+// Causal mask and online softmax of one key block's raw scores (two 32-key tiles, register
+// 4g+q of tile i is key kv0 + 32i + 8g + 4lh + q); returns P^T as the four k-step operands of
+// O^T += V^T P^T (slot s of k-step j: key 32(j/2) + 16(j%2) + 8(s/4) + 4lh + s%4).
+// Maxima are in log2 units and the score scale is folded into the exponent.  The
+// exponentials are taken against a reference maximum T.m that is raised only when some row
+// of the wave sees a block maximum more than 8 above its reference: then every row rescales
+// O and l to its new maximum (a wave-uniform branch; O lives in accumulation registers and a
+// rescale costs three instructions per element).  Otherwise p <= 2^8, well inside bf16 and
+// fp32 range.  O and l share the reference, so O / l is the softmax-weighted sum.
+constexpr float FA_RESCALE_SLACK = 8.0f;
+__device__ __forceinline__ void fa_softmax(FaTile& T, f32x16 (&sacc)[2], bf16x8 (&pf)[4], int kv0,
+                                           int lh, float scale_log2) {
+    if (kv0 + FA_BKV - 1 > T.p_lo) {  // the block reaches past some row's own position
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int key = kv0 + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+                if (key > T.qpos) sacc[i][e] = -INFINITY;
+            }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sacc[i][e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mx > T.m + FA_RESCALE_SLACK) != 0) {
+        const float m_new = fmaxf(T.m, mx);
+        const float corr = __builtin_amdgcn_exp2f(T.m - m_new);  // 0 while T.m = -inf
+        T.l *= corr;
+        // in groups of 8, so that few registers hold values on their way back
+#pragma unroll
+        for (int td = 0; td < 4; ++td)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) T.o[td][8 * h + e] *= corr;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        T.m = m_new;
+    }
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[i][e], scale_log2, -T.m));
+            psum += p;
+            sacc[i][e] = p;
+        }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            pf[j][s] = from_f32<bf16>(sacc[j >> 1][4 * (2 * (j & 1) + (s >> 2)) + (s & 3)]);
+    T.l += psum + __shfl_xor(psum, 32, 64);
+}
+
+// Workgroup = (sequence b, KV head g, query block qb): BQ = 128/group positions for the
+// group's query heads, 128 query rows; wave w owns rows 32w..32w+31 as one query tile.  Two
+// workgroups share a CU (64 KB of LDS each), so each SIMD runs two waves and one wave's
+// softmax overlaps the other's MFMAs.  Grid order: the first half of the workgroups take
+// the late (long) query blocks, latest first, the second half the matching early ones, so
+// that the two workgroups of a CU together cover about the same number of key blocks.
+__global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     bf16* __restrict__ out, int S, int start_pos, int H, int G, int seq_stride,
     float scale_log2, int nqb, int out_pack) {
     extern __shared__ u32x4 fa_smem[];
     const int group = H / G, BQ = FA_ROWS / group;
-    const int GB = gridDim.x / nqb;
-    const int qb = nqb - 1 - (int)blockIdx.x / GB;  // heaviest (latest) query blocks first
-    const int gb = (int)blockIdx.x % GB;
+    const int GB = G * (gridDim.x / (nqb * G));  // (b, g) pairs
+    const int heavy = (nqb + 1) / 2;             // blocks nqb-1 .. nqb-heavy come first
+    const int idx = (int)blockIdx.x;
+    const int qb = idx < heavy * GB ? nqb - 1 - idx / GB : (idx - heavy * GB) / GB;
+    const int gb = idx % GB;
     const int b = gb / G, g = gb % G;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, lr = lane & 31, lh = lane >> 5;
 
-    // this lane's query row
-    const int r = wave * 32 + lr;
-    const int hq = g * group + r / BQ;
-    const int sq = qb * BQ + r % BQ;
-    const bool qvalid = sq < S;
-    const int qpos = start_pos + sq;
-    const int p_lo = start_pos + qb * BQ;
-    const int p_hi = start_pos + min(S, qb * BQ + BQ) - 1;
-    const int ctx = p_hi + 1;                 // keys this block needs: 0..p_hi
-    const int nkb = (ctx + FA_BKV - 1) / FA_BKV;
-
-    bf16x8 qf[8];
-    {
-        const bf16* qrow = q + ((size_t)(b * S + (qvalid ? sq : 0)) * H + hq) * FA_D;
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk)
-            qf[kk] = qvalid ? *reinterpret_cast<const bf16x8*>(qrow + (kk * 2 + lh) * 8)
-                            : bf16x8{};
-    }
+    FaTile T;
+    fa_tile_init(T, q, qb, wave * 32 + lr, b, g, S, start_pos, H, group, BQ, lh);
+    const int nkb = T.nkb;
 
     const bf16* kbase = kc + ((size_t)b * G + g) * seq_stride * FA_D;
     const bf16* vbase = vc + ((size_t)b * G + g) * FA_D * seq_stride;
 
-    // loaders: K chunk idx = t + 256 i -> key row idx/16, 16-byte chunk idx%16;
-    //          V^T chunk idx = t + 256 i -> d row idx/8, keys 8*(idx%8)..+7
-    u32x4 kreg[4], vreg[4];
-    auto gload = [&](int kb) {
-        const int kv0 = kb * FA_BKV;
+    // Stage layout (LDS): K tile [64 keys][16 chunks of 16 B], chunk c of key row kr at slot
+    // c ^ (kr & 15); V^T tile [128 d][8 chunks of 16 B], chunk c of row d at slot c ^ (d & 7).
+    // Both arrive by direct global -> LDS copies, 1 KB (4 key rows / 8 d rows) per copy.
+    // Keys past the sequence's context are read too (whole 64-position blocks inside the
+    // cache); the causal mask gives them probability 0 and the cache holds finite values.
+    const unsigned lds0 = lds_addr(fa_smem);
+    auto issue = [&](int st, int kb) {
+        const bf16* ksrc = kbase + (size_t)kb * FA_BKV * FA_D;
+        const bf16* vsrc = vbase + (size_t)kb * FA_D * VT_BLOCK;
+        const unsigned dst = lds0 + st * FA_STAGE_BYTES;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int idx = t + 256 * i;
-            const int kr = idx >> 4, kcn = idx & 15;
-            kreg[i] = (kv0 + kr < ctx)
-                          ? *reinterpret_cast<const u32x4*>(kbase + (size_t)(kv0 + kr) * FA_D + kcn * 8)
-                          : u32x4{0, 0, 0, 0};
-            const int vd = idx >> 3, vcn = idx & 7;
-            const int key = kv0 + vcn * 8;
-            // kv0 is a multiple of the 64-position V^T block: key % 64 = 8 vcn
-            u32x4 v = (key < ctx) ? *reinterpret_cast<const u32x4*>(
-                                        vbase + ((size_t)kb * FA_D + vd) * VT_BLOCK + vcn * 8)
-                                  : u32x4{0, 0, 0, 0};
-            vreg[i] = mask_keys8(v, key, ctx);
+            const int ci = wave + 4 * i;
+            const int kr = 4 * ci + (lane >> 4), kcp = lane & 15;
+            lds_dma16(ksrc + kr * FA_D + ((kcp ^ (kr & 15)) * 8), dst + ci * 1024);
         }
-    };
-    auto swrite = [&](int st) {
-        u32x4* ks = fa_smem + st * (FA_STAGE_BYTES / 16);
-        uint2* vs = reinterpret_cast<uint2*>(ks + FA_KCH);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int idx = t + 256 * i;
-            const int kr = idx >> 4, kcn = idx & 15;
-            ks[kr * 16 + (kcn ^ (kr & 7))] = kreg[i];
-            const int vd = idx >> 3, vcn = idx & 7;
-            vs[vd * 16 + ((2 * vcn) ^ (vd & 15))] = make_uint2(vreg[i][0], vreg[i][1]);
-            vs[vd * 16 + ((2 * vcn + 1) ^ (vd & 15))] = make_uint2(vreg[i][2], vreg[i][3]);
+            const int ci = wave + 4 * i;
+            const int vd = 8 * ci + (lane >> 3), vcp = lane & 7;
+            lds_dma16(vsrc + vd * VT_BLOCK + ((vcp ^ (vd & 7)) * 8), dst + FA_KBYTES + ci * 1024);
         }
     };
 
-    f32x16 oacc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    gload(0);
+    issue(0, 0);
     for (int kb = 0; kb < nkb; ++kb) {
-        const int st = kb & 1;
-        swrite(st);
-        __syncthreads();
-        if (kb + 1 < nkb) gload(kb + 1);
-        const u32x4* ks = fa_smem + st * (FA_STAGE_BYTES / 16);
-        const uint2* vs = reinterpret_cast<const uint2*>(ks + FA_KCH);
+        // block kb has landed; the barrier also retires every wave's reads of the other slot
+        wait_vm_and_barrier<0>();
+        if (kb + 1 < nkb) issue((kb + 1) & 1, kb + 1);
+        const u32x4* ks = fa_smem + (kb & 1) * (FA_STAGE_BYTES / 16);
+        const uint2* vs = reinterpret_cast<const uint2*>(ks + FA_KBYTES / 16);
         const int kv0 = kb * FA_BKV;
 
-        // S^T = K Q^T: two 32-key tiles
+        // S^T = K Q^T: two 32-key tiles, K fragments read a quarter block ahead
         f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const int ch = (kk * 2 + lh) ^ (lr & 7);
+        for (int h = 0; h < 4; ++h) {
+            bf16x8 kf[2][2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, ks[(32 * i + lr) * 16 + ch]);
-                sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[i], 0, 0, 0);
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int kk = 2 * h + k2;
+                const int ch = (kk * 2 + lh) ^ (lr & 15);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    kf[k2][i] = __builtin_bit_cast(bf16x8, ks[(32 * i + lr) * 16 + ch]);
             }
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k2][i], T.qf[2 * h + k2], sacc[i], 0, 0, 0);
         }
-        // scale, mask, block max; register 4g+q of tile i is key kv0 + 32i + 8g + 4lh + q
-        const bool need_mask = kv0 + FA_BKV - 1 > p_lo;
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float sv = sacc[i][e] * scale_log2;
-                if (need_mask) {
-                    const int key = kv0 + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
-                    if (key > qpos) sv = -INFINITY;
-                }
-                sacc[i][e] = sv;
-                mx = fmaxf(mx, sv);
-            }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float corr = exp2f(m_run - m_new);
-        float psum = 0.0f;
         bf16x8 pf[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float p = exp2f(sacc[i][e] - m_new);
-                psum += p;
-                sacc[i][e] = p;
-            }
-        // P^T operand of k-step j (keys 32(j/2) + 16(j%2) + [0,16)): slot s of lane lh is
-        // key 32(j/2) + 16(j%2) + 8(s/4) + 4lh + s%4, i.e. registers 4(2(j%2) + s/4) + s%4
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int s = 0; s < 8; ++s)
-                pf[j][s] = from_f32<bf16>(sacc[j >> 1][4 * (2 * (j & 1) + (s >> 2)) + (s & 3)]);
-        psum += __shfl_xor(psum, 32, 64);
-        l_run = l_run * corr + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int td = 0; td < 4; ++td)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[td][e] *= corr;
-
-        // O^T += V^T P^T: V^T slot s of lane lh is key kbase_j + 8(s/4) + 4lh + s%4, i.e.
-        // the 8-byte chunks (kbase_j/4 + lh) and (kbase_j/4 + 2 + lh) of row d
+        fa_softmax(T, sacc, pf, kv0, lh, scale_log2);
+        // O^T += V^T P^T: V^T slot s of lane lh is key kbase_j + 8(s/4) + 4lh + s%4, i.e. the
+        // 8-byte halves lh of the 16-byte chunks kbase_j/8 and kbase_j/8 + 1 of row d
 #pragma unroll
         for (int td = 0; td < 4; ++td) {
             const int d = 32 * td + lr;
+            bf16x8 vf[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int c1 = (8 * (j >> 1) + 4 * (j & 1)) + lh;
-                const uint2 lo = vs[d * 16 + (c1 ^ (d & 15))];
-                const uint2 hi = vs[d * 16 + ((c1 + 2) ^ (d & 15))];
-                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-                oacc[td] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[j], oacc[td], 0, 0, 0);
+                const int c16 = 4 * (j >> 1) + 2 * (j & 1);
+                const uint2 lo = vs[d * 16 + ((c16 ^ (d & 7)) * 2) + lh];
+                const uint2 hi = vs[d * 16 + (((c16 + 1) ^ (d & 7)) * 2) + lh];
+                vf[j] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
             }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                T.o[td] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pf[j], T.o[td], 0, 0, 0);
         }
     }
 
-    if (!qvalid) return;
-    const float inv = 1.0f / l_run;
+    if (!T.valid) return;
+    const float inv = 1.0f / T.l;
 #pragma unroll
     for (int td = 0; td < 4; ++td)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
-            float v[4] = {oacc[td][4 * gg] * inv, oacc[td][4 * gg + 1] * inv,
-                          oacc[td][4 * gg + 2] * inv, oacc[td][4 * gg + 3] * inv};
-            store4(out + act_offset(b * S + sq, hq * FA_D + 32 * td + 8 * gg + 4 * lh, H * FA_D,
-                                    out_pack),
+            float v[4] = {T.o[td][4 * gg] * inv, T.o[td][4 * gg + 1] * inv,
+                          T.o[td][4 * gg + 2] * inv, T.o[td][4 * gg + 3] * inv};
+            store4(out + act_offset(b * S + T.sq, T.hq * FA_D + 32 * td + 8 * gg + 4 * lh,
+                                    H * FA_D, out_pack),
                    v);
         }
 }

@@ -54,5 +54,28 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane i
+// of the wave writes LDS bytes [lds + 16 i, lds + 16 i + 16).  Issued from inline asm so
+// that the compiler does not serialise every later LDS read behind it; completion is
+// tracked by hand with s_waitcnt vmcnt (the copy has no VGPR result).
+__device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds_byte) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "v"(gptr)
+                 : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding, then
+// synchronise the workgroup.
+template <int N>
+__device__ __forceinline__ void wait_vm_and_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+// LDS byte address of a __shared__ (address space 3) pointer, for the m0 of lds_dma16.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
 // Device error flags, OR-ed into a word of the workspace and read by llama_sync_status.
 enum : uint32_t { DEVERR_TOKEN_RANGE = 1u, DEVERR_NAN_LOGIT = 2u };

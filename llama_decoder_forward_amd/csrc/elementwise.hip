@@ -229,6 +229,20 @@ hipError_t zero_u32(uint32_t* p, int n, hipStream_t s) {
     return hipGetLastError();
 }
 
+__global__ void zero_bytes_kernel(u32x4* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+hipError_t zero_bytes(void* p, size_t bytes, hipStream_t s) {
+    if (bytes % 16 != 0 || ((uintptr_t)p % 16) != 0) return hipErrorInvalidValue;
+    const size_t n = bytes / 16;
+    if (n == 0) return hipSuccess;
+    const size_t want = (n + 255) / 256;
+    zero_bytes_kernel<<<(unsigned)(want < 8192 ? want : 8192), 256, 0, s>>>((u32x4*)p, n);
+    return hipGetLastError();
+}
+
 __global__ void copy_tokens_kernel(const int* src, int* dst, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) dst[i] = src[i];

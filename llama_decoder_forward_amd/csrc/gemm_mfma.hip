@@ -22,22 +22,6 @@ hipError_t simt_qkv(const GemmArgs<void>& g, const EpiQKV<void>& e, hipStream_t 
 
 namespace {
 
-// Direct global -> LDS copy of 16 bytes per lane (gfx950 global_load_lds_dwordx4): lane i
-// of the wave writes LDS bytes [lds + 16 i, lds + 16 i + 16).  Issued from inline asm so
-// that the compiler does not serialise every later LDS read behind it; completion is
-// tracked by hand with s_waitcnt vmcnt (the copy has no VGPR result).
-__device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds_byte) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                 :
-                 : "s"(__builtin_amdgcn_readfirstlane(lds_byte)), "v"(gptr)
-                 : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm_and_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
-}
-
 // Block tile BN weight rows x BM tokens x BK, STAGES-deep LDS ring; the grid covers weight
 // rows [n_begin, N) and all M tokens.  LDS row = BK bf16
 // (RB bytes) split in 16-byte chunks; chunk c of row r is stored at c ^ swz(r) so that the

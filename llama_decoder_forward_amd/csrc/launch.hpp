@@ -20,6 +20,8 @@ hipError_t argmax(const float* logits, int rows, int V, int* out, int* out2, int
                   const int* counter, void* scratch, uint32_t* err, hipStream_t s);
 hipError_t bump_counters(int* pos, int* step, hipStream_t s);
 hipError_t zero_u32(uint32_t* p, int n, hipStream_t s);
+// fill `bytes` bytes (a multiple of 16, 16-byte aligned) with zeros
+hipError_t zero_bytes(void* p, size_t bytes, hipStream_t s);
 hipError_t copy_tokens(const int* src, int* dst, int n, hipStream_t s);
 hipError_t set_counters(int* pos, int pos_value, int* step, hipStream_t s);
 
