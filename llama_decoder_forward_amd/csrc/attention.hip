@@ -355,7 +355,8 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
 // 64-key block holds in MFMA row i the key 32j + 8(i/4) + 4h + i%4, so that the result
 // register e of lane (c, kq) is key 32j + 8kq + 4h + e; the P^T operand of k-step j is then
 // keys 32j + 8kq + 0..7 of the lane's own registers, and the matching V^T operand is one
-// 16-byte run of row d.  Along d, lane kq supplies d = 32kq + 8jj .. +7 for k-step jj.
+// 16-byte run of row d.  Along d, lane kq supplies d = 32jj + 8kq .. +7 for k-step jj, so
+// the four lanes of a key row read 64 contiguous bytes per load.
 // ------------------------------------------------------------------------------------
 constexpr int DEC_BLOCK = 64;  // keys per wave per iteration
 
@@ -378,10 +379,10 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
     bf16x8 qf[4];
     {
         const bool real = col < group;
-        const bf16* qrow = q + ((size_t)b * H + g * group + (real ? col : 0)) * FA_D + 32 * kq;
+        const bf16* qrow = q + ((size_t)b * H + g * group + (real ? col : 0)) * FA_D + 8 * kq;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-            qf[jj] = real ? *reinterpret_cast<const bf16x8*>(qrow + 8 * jj) : bf16x8{};
+            qf[jj] = real ? *reinterpret_cast<const bf16x8*>(qrow + 32 * jj) : bf16x8{};
     }
     const bf16* kbase = kc + ((size_t)b * G + g) * seq_stride * FA_D;
     const bf16* vbase = vc + ((size_t)b * G + g) * FA_D * seq_stride;
@@ -396,10 +397,10 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int key = kb + 32 * (t >> 1) + 8 * (col >> 2) + 4 * (t & 1) + (col & 3);
-            const bf16* src = kbase + (size_t)key * FA_D + 32 * kq;
+            const bf16* src = kbase + (size_t)key * FA_D + 8 * kq;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-                kr[t][jj] = (key < c1) ? *reinterpret_cast<const u32x4*>(src + 8 * jj) : u32x4{0, 0, 0, 0};
+                kr[t][jj] = (key < c1) ? *reinterpret_cast<const u32x4*>(src + 32 * jj) : u32x4{0, 0, 0, 0};
         }
         // kb is a multiple of the 64-position V^T block
         const bf16* vblk = vbase + (size_t)(kb / VT_BLOCK) * FA_D * VT_BLOCK;
@@ -423,28 +424,31 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
                 sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8, kr[t][jj]), qf[jj], sacc[t], 0, 0, 0);
         }
+        if (kb + DEC_BLOCK > c1) {  // the block runs past the context
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = kb + 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + e;
+                    if (key >= c1) sacc[t][e] = -INFINITY;
+                }
+        }
         float mx = -INFINITY;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int key = kb + 32 * (t >> 1) + 8 * kq + 4 * (t & 1) + e;
-                float sv = sacc[t][e] * scale_log2;
-                if (key >= c1) sv = -INFINITY;
-                sacc[t][e] = sv;
-                mx = fmaxf(mx, sv);
-            }
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sacc[t][e]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float corr = exp2f(m_run - m_new);
+        const float m_new = fmaxf(m_run, mx * scale_log2);  // log2 units
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_new);
         float psum = 0.0f;
         bf16x8 pf[2];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float p = exp2f(sacc[t][e] - m_new);
+                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][e], scale_log2, -m_new));
                 psum += p;
                 pf[t >> 1][4 * (t & 1) + e] = from_f32<bf16>(p);
             }
