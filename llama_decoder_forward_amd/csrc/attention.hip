@@ -150,9 +150,10 @@ __device__ __forceinline__ void fa_tile_init(FaTile& T, const bf16* __restrict__
     T.l = 0.0f;
 }
 
-// Causal mask and online softmax of one key block's raw scores (two 32-key tiles, register
-// 4g+q of tile i is key kv0 + 32i + 8g + 4lh + q); returns P^T as the four k-step operands of
-// O^T += V^T P^T (slot s of k-step j: key 32(j/2) + 16(j%2) + 8(s/4) + 4lh + s%4).
+// Causal mask and online softmax of one key block's raw scores (two 32-key tiles; with the
+// key order of the S^T tiles, register e of tile i is key kv0 + 32i + 16(e/8) + 8lh + e%8);
+// returns P^T as the four k-step operands of O^T += V^T P^T: k-step j takes registers
+// 8(j%2)..+7 of tile j/2, the keys 32(j/2) + 16(j%2) + 8lh + 0..7.
 // Maxima are in log2 units and the score scale is folded into the exponent.  The
 // exponentials are taken against a reference maximum T.m that is raised only when some row
 // of the wave sees a block maximum more than 8 above its reference: then every row rescales
@@ -167,7 +168,7 @@ __device__ __forceinline__ void fa_softmax(FaTile& T, f32x16 (&sacc)[2], bf16x8 
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int key = kv0 + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+                const int key = kv0 + 32 * i + 16 * (e >> 3) + 8 * lh + (e & 7);
                 if (key > T.qpos) sacc[i][e] = -INFINITY;
             }
     }
@@ -204,8 +205,7 @@ __device__ __forceinline__ void fa_softmax(FaTile& T, f32x16 (&sacc)[2], bf16x8 
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            pf[j][s] = from_f32<bf16>(sacc[j >> 1][4 * (2 * (j & 1) + (s >> 2)) + (s & 3)]);
+        for (int s = 0; s < 8; ++s) pf[j][s] = from_f32<bf16>(sacc[j >> 1][8 * (j & 1) + s]);
     T.l += psum + __shfl_xor(psum, 32, 64);
 }
 
@@ -237,8 +237,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     const bf16* vbase = vc + ((size_t)b * G + g) * FA_D * seq_stride;
 
     // Stage layout (LDS): K tile [64 keys][16 chunks of 16 B], chunk c of key row kr at slot
-    // c ^ (kr & 15); V^T tile [128 d][8 chunks of 16 B], chunk c of row d at slot c ^ (d & 7).
-    // Both arrive by direct global -> LDS copies, 1 KB (4 key rows / 8 d rows) per copy.
+    // c ^ (kr & 15); V^T tile [128 d][8 chunks of 16 B], chunk c of row d at slot
+    // c ^ ((d >> 1) & 7).  Both arrive by direct global -> LDS copies, 1 KB (4 key rows /
+    // 8 d rows) per copy; both operand reads below are conflict-free 16-byte reads.
     // Keys past the sequence's context are read too (whole 64-position blocks inside the
     // cache); the causal mask gives them probability 0 and the cache holds finite values.
     const unsigned lds0 = lds_addr(fa_smem);
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
         for (int i = 0; i < 4; ++i) {
             const int ci = wave + 4 * i;
             const int vd = 8 * ci + (lane >> 3), vcp = lane & 7;
-            lds_dma16(vsrc + vd * VT_BLOCK + ((vcp ^ (vd & 7)) * 8), dst + FA_KBYTES + ci * 1024);
+            lds_dma16(vsrc + vd * VT_BLOCK + ((vcp ^ ((vd >> 1) & 7)) * 8), dst + FA_KBYTES + ci * 1024);
         }
     };
 
@@ -266,10 +267,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
         wait_vm_and_barrier<0>();
         if (kb + 1 < nkb) issue((kb + 1) & 1, kb + 1);
         const u32x4* ks = fa_smem + (kb & 1) * (FA_STAGE_BYTES / 16);
-        const uint2* vs = reinterpret_cast<const uint2*>(ks + FA_KBYTES / 16);
+        const u32x4* vs = ks + FA_KBYTES / 16;
         const int kv0 = kb * FA_BKV;
 
-        // S^T = K Q^T: two 32-key tiles, K fragments read a quarter block ahead
+        // S^T = K Q^T: two 32-key tiles, K fragments read a quarter block ahead.  MFMA row r
+        // of tile i is key 32i + pi(r), pi(r) = 16(r/16) + 8((r/4)%2) + 4((r/8)%2) + r%4, so
+        // that each lane's eight P values of one P.V k-step are eight consecutive keys.
+        const int krow = 16 * (lr >> 4) + 8 * ((lr >> 2) & 1) + 4 * ((lr >> 3) & 1) + (lr & 3);
         f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
@@ -277,10 +281,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const int kk = 2 * h + k2;
-                const int ch = (kk * 2 + lh) ^ (lr & 15);
+                const int ch = (kk * 2 + lh) ^ (krow & 15);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    kf[k2][i] = __builtin_bit_cast(bf16x8, ks[(32 * i + lr) * 16 + ch]);
+                    kf[k2][i] = __builtin_bit_cast(bf16x8, ks[(32 * i + krow) * 16 + ch]);
             }
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2)
@@ -290,19 +294,15 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
         }
         bf16x8 pf[4];
         fa_softmax(T, sacc, pf, kv0, lh, scale_log2);
-        // O^T += V^T P^T: V^T slot s of lane lh is key kbase_j + 8(s/4) + 4lh + s%4, i.e. the
-        // 8-byte halves lh of the 16-byte chunks kbase_j/8 and kbase_j/8 + 1 of row d
+        // O^T += V^T P^T: the V^T operand of k-step j for lane lh is keys 16j + 8lh .. +7 of
+        // row d, the 16-byte chunk 2j + lh
 #pragma unroll
         for (int td = 0; td < 4; ++td) {
             const int d = 32 * td + lr;
             bf16x8 vf[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int c16 = 4 * (j >> 1) + 2 * (j & 1);
-                const uint2 lo = vs[d * 16 + ((c16 ^ (d & 7)) * 2) + lh];
-                const uint2 hi = vs[d * 16 + (((c16 + 1) ^ (d & 7)) * 2) + lh];
-                vf[j] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-            }
+            for (int j = 0; j < 4; ++j)
+                vf[j] = __builtin_bit_cast(bf16x8, vs[d * 8 + ((2 * j + lh) ^ ((d >> 1) & 7))]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 T.o[td] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pf[j], T.o[td], 0, 0, 0);
