@@ -38,6 +38,30 @@ def prefill_flops(spec, B: int, S: int) -> float:
     return spec.n_layers * (B * S * per_tok + attn) + 2 * B * spec.vocab_size * D
 
 
+def chunk_prefill_flops(spec, S: int, start_pos: int) -> float:
+    """Algorithmic FLOPs of one sequence's S tokens at positions start_pos..: layer GEMMs,
+    attention of each token over positions 0..its own, the last token's vocabulary row."""
+    D, H, G, d, F = spec.dim, spec.n_heads, spec.n_kv_heads, spec.head_dim, spec.ffn_hidden
+    per_tok = 2 * (D * (H + 2 * G) * d + H * d * D + 3 * D * F)
+    keys = S * start_pos + S * (S + 1) / 2
+    return spec.n_layers * (S * per_tok + 4 * H * d * keys) + 2 * spec.vocab_size * D
+
+
+def ragged_decode_bytes(spec, positions, steps: int) -> float:
+    """decode_bytes for sequences at their own positions (context = position + 1)."""
+    D, H, G, d, F, V = (spec.dim, spec.n_heads, spec.n_kv_heads, spec.head_dim,
+                        spec.ffn_hidden, spec.vocab_size)
+    w_layer = 2 * (D * (H + 2 * G) * d + H * d * D + 3 * D * F + 2 * D)
+    weights = spec.n_layers * w_layer + 2 * V * D + 2 * D
+    B = len(positions)
+    total = 0.0
+    for k in range(steps):
+        ctx = sum(p + 1 + k for p in positions)
+        total += (weights + spec.n_layers * G * ctx * d * 2 * 2
+                  + spec.n_layers * B * G * d * 2 * 2 + B * V * 4)
+    return total
+
+
 def decode_bytes(spec, B: int, ctx_first: int, steps: int) -> float:
     """Algorithmic HBM bytes of `steps` decode steps: every weight once per step, the KV
     cache read over the context, the new K/V written, the logits written."""
@@ -285,6 +309,63 @@ def main() -> int:
                          "avg_launch_ms": a_avg, "launches": a_n},
             "tokens_head": out[:4, 0].tolist(),
         }
+
+        # ragged decode: every sequence at its own position (llama_decode_step_ragged), the
+        # contexts spread evenly over [dec_ctx/2, dec_ctx)
+        rpos = [dec_ctx - 1 - (b * dec_ctx) // (2 * dec_B) for b in range(dec_B)]
+        r_steps = 8 if args.profile_only else 32
+        pos_dev = torch.tensor(rpos, dtype=torch.int32, device="cuda")
+        cur = first.clone()
+        for _ in range(2):                                # warmup (rewrites the same entries)
+            m.decode_step_ragged(cur, pos_dev, want_logits=False)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for _ in range(r_steps):
+            cur, _ = m.decode_step_ragged(cur, pos_dev, want_logits=False)
+            pos_dev += 1
+        stop.record(stream)
+        torch.cuda.synchronize()
+        rms = start.elapsed_time(stop)
+        m.sync_status()
+        rbytes = ragged_decode_bytes(spec, rpos, r_steps)
+        log(f"ragged decode: {rms / r_steps:.3f} ms/step")
+        result["ragged_decode"] = {
+            "value": dec_B * r_steps / (rms * 1e-3), "unit": "tokens/s",
+            "ms_per_step": rms / r_steps, "steps": r_steps, "batch": dec_B,
+            "context": [min(rpos) + 1, max(rpos) + r_steps],
+            "workload": f"llama3-8b-shaped greedy decode of {dec_B} sequences at their own "
+                        f"positions ({min(rpos)}..{max(rpos)} at the first step), "
+                        f"{r_steps} steps (llama_decode_step_ragged, eager)",
+            "hbm_gbs": rbytes / (rms * 1e-3) / 1e9,
+            "hbm_frac": rbytes / (rms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        }
+
+        # chunked prefill: the second S tokens of a sequence, at positions S..2S-1, after a
+        # prefix of S (llama_prefill_at); each call rewrites the same cache entries
+        if 2 * S <= max_seq:
+            c_toks = torch.from_numpy(syn.tokens(seed + 1, 1, 2 * S, spec.vocab_size)).cuda()
+            m.prefill(c_toks[:, :S].contiguous())
+            chunk = c_toks[:, S:].contiguous()
+            c_steps = 1 if args.profile_only else max(1, args.steps)
+            m.prefill(chunk, start_pos=S)
+            torch.cuda.synchronize()
+            start.record(stream)
+            for _ in range(c_steps):
+                m.prefill(chunk, start_pos=S)
+            stop.record(stream)
+            torch.cuda.synchronize()
+            cms = start.elapsed_time(stop) / c_steps
+            m.sync_status()
+            cfl = chunk_prefill_flops(spec, S, S)
+            log(f"chunked prefill: {cms:.2f} ms per {S}-token chunk at start_pos {S}")
+            result["chunked_prefill"] = {
+                "value": S / (cms * 1e-3), "unit": "tokens/s", "ms_per_step": cms,
+                "steps": c_steps,
+                "workload": f"llama3-8b-shaped prefill of tokens {S}..{2 * S - 1} of one "
+                            f"sequence after a {S}-token prefix (llama_prefill_at)",
+                "mfma_frac": cfl / (cms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "tflops": cfl / (cms * 1e-3) / 1e12,
+            }
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline and not args.profile_only:

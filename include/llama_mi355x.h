@@ -126,6 +126,18 @@ llama_status llama_init_weights(const llama_config *cfg, const llama_weights *we
 llama_status llama_prefill(llama_model *m, const int32_t *tokens, int32_t B, int32_t S,
                            float *logits, int32_t all_positions, hipStream_t stream);
 
+/* Prefill continued from position start_pos (chunked prefill into an existing cache): the
+ * S tokens [B,S] of each of B sequences sit at positions start_pos..start_pos+S-1, their keys
+ * and values are written to the cache there, and each attends causally to cache positions
+ * 0..its own position, which needs the cache filled at 0..start_pos-1 by earlier calls
+ * (article, section 多头注意力 for the causal mask; the cache itself is the Hacker News
+ * thread's pre-allocated max_seq_len x max_batch_size buffer).  Logits as llama_prefill;
+ * llama_prefill is this call with start_pos = 0.  Needs start_pos >= 0,
+ * start_pos + S <= max_seq, B <= max_batch, B*S <= max_tokens; CAPACITY otherwise. */
+llama_status llama_prefill_at(llama_model *m, const int32_t *tokens, int32_t B, int32_t S,
+                              int32_t start_pos, float *logits, int32_t all_positions,
+                              hipStream_t stream);
+
 /* One KV-cache decode step: token tokens[b] of sequence b sits at position pos, its key
  * and value are written to the cache at pos, and it attends to cache positions 0..pos.
  * Writes next_tokens[b] = argmax of its logits (lowest index on ties) and, if logits is
@@ -133,6 +145,17 @@ llama_status llama_prefill(llama_model *m, const int32_t *tokens, int32_t B, int
  * cache filled at 0..pos-1 by earlier calls.  tokens and next_tokens may alias. */
 llama_status llama_decode_step(llama_model *m, const int32_t *tokens, int32_t B, int32_t pos,
                                float *logits, int32_t *next_tokens, hipStream_t stream);
+
+/* Decode step of a ragged batch: sequence b's token tokens[b] sits at its own position
+ * positions[b] (device memory, int32 [B]); its key and value are written at that position
+ * and it attends to its cache positions 0..positions[b] (so sequences of different lengths
+ * decode together; cache entries past a sequence's position are ignored).  Otherwise as
+ * llama_decode_step.  positions is read on the device: a value outside [0, max_seq) makes
+ * llama_sync_status report INVALID_ARG; that sequence's cache is left untouched and its
+ * outputs are unspecified, and no access leaves the buffers. */
+llama_status llama_decode_step_ragged(llama_model *m, const int32_t *tokens, int32_t B,
+                                      const int32_t *positions, float *logits,
+                                      int32_t *next_tokens, hipStream_t stream);
 
 /* n_steps greedy decode steps starting with tokens[b] at position pos: step k runs at
  * position pos+k on the previous step's argmax.  The position and step index live in
@@ -153,7 +176,8 @@ llama_status llama_layer_forward(llama_model *m, int32_t layer, const float *x_i
 
 /* Synchronise the stream, then report device-detected input errors since the last check
  * (token ids outside [0,V) give INVALID_ARG; their embedding rows are zero; NaN logits in
- * argmax give INVALID_ARG) and clear them. */
+ * argmax give INVALID_ARG; so do ragged-decode positions outside [0, max_seq)) and clear
+ * them. */
 llama_status llama_sync_status(llama_model *m, hipStream_t stream);
 
 /* Kernel classes of the forward pass, for llama_profile_kernel. */

@@ -48,8 +48,9 @@ class LlamaWeights(ctypes.Structure):
 
 
 EXPORTS = ["llama_kv_cache_bytes", "llama_workspace_bytes", "llama_init_weights", "llama_prefill",
-           "llama_decode_step", "llama_generate", "llama_layer_forward", "llama_sync_status",
-           "llama_free", "llama_last_error", "llama_profile_kernel", "llama_profile_read"]
+           "llama_prefill_at", "llama_decode_step", "llama_decode_step_ragged", "llama_generate",
+           "llama_layer_forward", "llama_sync_status", "llama_free", "llama_last_error",
+           "llama_profile_kernel", "llama_profile_read"]
 
 KERNELS = {"none": 0, "qkv": 1, "attention": 2, "wo": 3, "ffn_up": 4, "ffn_down": 5,
            "lm_head": 6, "rmsnorm": 7}
@@ -73,7 +74,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.llama_workspace_bytes.restype = Z
     lib.llama_init_weights.argtypes = [F(LlamaConfig), F(LlamaWeights), P, Z, P, Z, F(P)]
     lib.llama_prefill.argtypes = [P, P, I, I, P, I, P]
+    lib.llama_prefill_at.argtypes = [P, P, I, I, I, P, I, P]
     lib.llama_decode_step.argtypes = [P, P, I, I, P, P, P]
+    lib.llama_decode_step_ragged.argtypes = [P, P, I, P, P, P, P]
     lib.llama_generate.argtypes = [P, P, I, I, I, P, P, P]
     lib.llama_layer_forward.argtypes = [P, I, P, P, I, I, I, P]
     lib.llama_sync_status.argtypes = [P, P]
@@ -83,9 +86,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.llama_free.restype = None
     lib.llama_last_error.argtypes = []
     lib.llama_last_error.restype = ctypes.c_char_p
-    for fn in ("llama_init_weights", "llama_prefill", "llama_decode_step", "llama_generate",
-               "llama_layer_forward", "llama_sync_status", "llama_profile_kernel",
-               "llama_profile_read"):
+    for fn in ("llama_init_weights", "llama_prefill", "llama_prefill_at", "llama_decode_step",
+               "llama_decode_step_ragged", "llama_generate", "llama_layer_forward",
+               "llama_sync_status", "llama_profile_kernel", "llama_profile_read"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -161,15 +164,21 @@ class Model:
         self.seq_stride = (max_seq + 63) // 64 * 64
 
     # -------------------------------------------------------------- calls
-    def prefill(self, tokens: torch.Tensor, all_positions: bool = False, logits=None, stream=None):
+    def prefill(self, tokens: torch.Tensor, all_positions: bool = False, logits=None, stream=None,
+                start_pos: int = 0):
+        """Prefill [B, S] tokens at positions start_pos.. (llama_prefill / llama_prefill_at)."""
         B, S = tokens.shape
         assert tokens.dtype == torch.int32 and tokens.is_contiguous()
         V = self.spec.vocab_size
         if logits is None:
             shape = (B, S, V) if all_positions else (B, V)
             logits = torch.empty(shape, dtype=torch.float32, device=self.device)
-        check(self.lib.llama_prefill(self.handle, _ptr(tokens), B, S, _ptr(logits),
-                                     int(all_positions), _stream(stream)))
+        if start_pos == 0:
+            check(self.lib.llama_prefill(self.handle, _ptr(tokens), B, S, _ptr(logits),
+                                         int(all_positions), _stream(stream)))
+        else:
+            check(self.lib.llama_prefill_at(self.handle, _ptr(tokens), B, S, start_pos,
+                                            _ptr(logits), int(all_positions), _stream(stream)))
         return logits
 
     def decode_step(self, tokens: torch.Tensor, pos: int, want_logits: bool = True,
@@ -183,6 +192,22 @@ class Model:
         check(self.lib.llama_decode_step(self.handle, _ptr(tokens), B, pos,
                                          _ptr(logits) if want_logits else None,
                                          _ptr(next_tokens), _stream(stream)))
+        return next_tokens, (logits if want_logits else None)
+
+    def decode_step_ragged(self, tokens: torch.Tensor, positions: torch.Tensor,
+                           want_logits: bool = True, next_tokens=None, logits=None, stream=None):
+        """One decode step with a position per sequence (device int32 [B])."""
+        B = tokens.shape[0]
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+        assert positions.dtype == torch.int32 and positions.is_contiguous() and positions.is_cuda
+        assert positions.shape == (B,)
+        if next_tokens is None:
+            next_tokens = torch.empty(B, dtype=torch.int32, device=self.device)
+        if want_logits and logits is None:
+            logits = torch.empty((B, self.spec.vocab_size), dtype=torch.float32, device=self.device)
+        check(self.lib.llama_decode_step_ragged(self.handle, _ptr(tokens), B, _ptr(positions),
+                                                _ptr(logits) if want_logits else None,
+                                                _ptr(next_tokens), _stream(stream)))
         return next_tokens, (logits if want_logits else None)
 
     def generate(self, tokens: torch.Tensor, pos: int, n_steps: int, want_logits: bool = False,

@@ -194,7 +194,7 @@ lk::GemmArgs<void> gemm_args(llama_model* m, const void* A, int lda, const void*
 
 // One decoder layer on rows = B*S tokens (article, sections 构建Transformer层 to 前馈神经网络层).
 llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int B, int S,
-                       int start_pos, const int* pos_dev, int max_ctx, bool decode,
+                       int start_pos, const int* pos_dev, int pos_stride, int max_ctx, bool decode,
                        hipStream_t s) {
     const llama_config& c = m->cfg;
     const llama_layer_weights& w = m->layers[l];
@@ -214,14 +214,14 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
     lk::GemmArgs<void> qkv = gemm_args(m, m->h(), D, w.wq, T, Nq + 2 * Nk, D);
     qkv.W = WeightRows<void>{w.wq, w.wk, w.wv, Nq, Nq + Nk, D};
     EpiQKV<void> eq{m->q(), m->kc(l), m->vc(l), m->rope(), Nq, Nk, d, S, start_pos, G,
-                    m->seq_stride, pos_dev};
+                    m->seq_stride, pos_dev, pos_stride, c.max_seq};
     {
         ProfScope ps(m, LLAMA_KERNEL_QKV, s);
         HIP_TRY(lk::gemm_qkv(m->dt, qkv, eq, s));
     }
 
     lk::AttnArgs aa{m->q(), m->kc(l), m->vc(l), m->attn(), pk_wo, B, S, start_pos, H, G, d,
-                    m->seq_stride, pos_dev, m->partials(), max_ctx};
+                    m->seq_stride, pos_dev, pos_stride, c.max_seq, m->partials(), max_ctx};
     {
         ProfScope ps(m, LLAMA_KERNEL_ATTENTION, s);
         if (decode) HIP_TRY(lk::attention_decode(m->dt, aa, s));
@@ -270,12 +270,14 @@ llama_status run_head(llama_model* m, int rows, int step, int offset, float* log
 
 // One decode step of B rows; position from `pos` or, if pos_dev is set, from device memory.
 llama_status run_decode_step(llama_model* m, const int32_t* tokens, int B, int pos,
-                             const int* pos_dev, int max_ctx, float* logits, int32_t* next,
+                             const int* pos_dev, int pos_stride, int max_ctx, float* logits,
+                             int32_t* next,
                              int32_t* log_out, const int* step_ctr, hipStream_t s) {
     const llama_config& c = m->cfg;
     HIP_TRY(lk::embed(m->dt, tokens, m->tok_embeddings, m->x(), B, c.dim, c.vocab_size, m->deverr(), s));
     for (int l = 0; l < c.n_layers; ++l) {
-        llama_status st = run_layer(m, l, m->x(), m->x(), B, 1, pos, pos_dev, max_ctx, true, s);
+        llama_status st =
+            run_layer(m, l, m->x(), m->x(), B, 1, pos, pos_dev, pos_stride, max_ctx, true, s);
         if (st != LLAMA_OK) return st;
     }
     float* lg = logits ? logits : m->logits_scratch();
@@ -340,13 +342,15 @@ llama_status llama_init_weights(const llama_config* cfg, const llama_weights* w,
     return LLAMA_OK;
 }
 
-llama_status llama_prefill(llama_model* m, const int32_t* tokens, int32_t B, int32_t S,
-                           float* logits, int32_t all_positions, hipStream_t s) {
+llama_status llama_prefill_at(llama_model* m, const int32_t* tokens, int32_t B, int32_t S,
+                              int32_t start_pos, float* logits, int32_t all_positions,
+                              hipStream_t s) {
     if (!m || !tokens || !logits) return fail(LLAMA_ERR_INVALID_ARG, "NULL model, tokens or logits");
     const llama_config& c = m->cfg;
     if (B <= 0 || S <= 0) return fail(LLAMA_ERR_SHAPE, "B and S must be positive (B=%d S=%d)", B, S);
     if (B > c.max_batch) return fail(LLAMA_ERR_CAPACITY, "B=%d > max_batch=%d", B, c.max_batch);
-    if (S > c.max_seq) return fail(LLAMA_ERR_CAPACITY, "S=%d > max_seq=%d", S, c.max_seq);
+    if (start_pos < 0 || (long long)start_pos + S > c.max_seq)
+        return fail(LLAMA_ERR_CAPACITY, "start_pos=%d + S=%d exceeds max_seq=%d", start_pos, S, c.max_seq);
     if ((long long)B * S > c.max_tokens)
         return fail(LLAMA_ERR_CAPACITY, "B*S=%lld > max_tokens=%d", (long long)B * S, c.max_tokens);
     llama_status st = ensure_rope(m, s);
@@ -354,11 +358,16 @@ llama_status llama_prefill(llama_model* m, const int32_t* tokens, int32_t B, int
     const int T = B * S;
     HIP_TRY(lk::embed(m->dt, tokens, m->tok_embeddings, m->x(), T, c.dim, c.vocab_size, m->deverr(), s));
     for (int l = 0; l < c.n_layers; ++l) {
-        st = run_layer(m, l, m->x(), m->x(), B, S, 0, nullptr, S, false, s);
+        st = run_layer(m, l, m->x(), m->x(), B, S, start_pos, nullptr, 0, start_pos + S, false, s);
         if (st != LLAMA_OK) return st;
     }
     if (all_positions) return run_head(m, T, 1, 0, logits, s);
     return run_head(m, B, S, S - 1, logits, s);
+}
+
+llama_status llama_prefill(llama_model* m, const int32_t* tokens, int32_t B, int32_t S,
+                           float* logits, int32_t all_positions, hipStream_t s) {
+    return llama_prefill_at(m, tokens, B, S, 0, logits, all_positions, s);
 }
 
 llama_status llama_decode_step(llama_model* m, const int32_t* tokens, int32_t B, int32_t pos,
@@ -370,7 +379,25 @@ llama_status llama_decode_step(llama_model* m, const int32_t* tokens, int32_t B,
     if (pos < 0 || pos >= c.max_seq) return fail(LLAMA_ERR_CAPACITY, "pos=%d outside [0, max_seq=%d)", pos, c.max_seq);
     llama_status st = ensure_rope(m, s);
     if (st != LLAMA_OK) return st;
-    return run_decode_step(m, tokens, B, pos, nullptr, pos + 1, logits, next_tokens, nullptr, nullptr, s);
+    return run_decode_step(m, tokens, B, pos, nullptr, 0, pos + 1, logits, next_tokens, nullptr,
+                           nullptr, s);
+}
+
+llama_status llama_decode_step_ragged(llama_model* m, const int32_t* tokens, int32_t B,
+                                      const int32_t* positions, float* logits,
+                                      int32_t* next_tokens, hipStream_t s) {
+    if (!m || !tokens || !positions || !next_tokens)
+        return fail(LLAMA_ERR_INVALID_ARG, "NULL model, tokens, positions or next_tokens");
+    const llama_config& c = m->cfg;
+    if (B <= 0) return fail(LLAMA_ERR_SHAPE, "B must be positive (B=%d)", B);
+    if (B > c.max_batch) return fail(LLAMA_ERR_CAPACITY, "B=%d > max_batch=%d", B, c.max_batch);
+    llama_status st = ensure_rope(m, s);
+    if (st != LLAMA_OK) return st;
+    // positions live on the device: checked there (flag for llama_sync_status), and every
+    // kernel replaces an out-of-range one by 0, so that no access leaves the cache
+    HIP_TRY(lk::check_positions(positions, B, c.max_seq, m->deverr(), s));
+    return run_decode_step(m, tokens, B, 0, positions, 1, c.max_seq, logits, next_tokens, nullptr,
+                           nullptr, s);
 }
 
 llama_status llama_generate(llama_model* m, const int32_t* tokens, int32_t B, int32_t pos,
@@ -390,7 +417,7 @@ llama_status llama_generate(llama_model* m, const int32_t* tokens, int32_t B, in
     // The step reads its position and step index from device memory, so the same launch
     // sequence repeats with no host round trip; the argmax of each step feeds the next.
     for (int k = 0; k < n_steps; ++k) {
-        st = run_decode_step(m, m->tokbuf(), B, 0, m->pos_ctr(), max_ctx,
+        st = run_decode_step(m, m->tokbuf(), B, 0, m->pos_ctr(), 0, max_ctx,
                              logits ? logits + (size_t)k * B * c.vocab_size : nullptr,
                              m->tokbuf(), out_tokens, m->step_ctr(), s);
         if (st != LLAMA_OK) return st;
@@ -413,7 +440,7 @@ llama_status llama_layer_forward(llama_model* m, int32_t layer, const float* x_i
         return fail(LLAMA_ERR_CAPACITY, "B*S=%lld > max_tokens=%d", (long long)B * S, c.max_tokens);
     llama_status st = ensure_rope(m, s);
     if (st != LLAMA_OK) return st;
-    return run_layer(m, layer, x_in, x_out, B, S, start_pos, nullptr, start_pos + S, false, s);
+    return run_layer(m, layer, x_in, x_out, B, S, start_pos, nullptr, 0, start_pos + S, false, s);
 }
 
 llama_status llama_sync_status(llama_model* m, hipStream_t s) {
@@ -424,9 +451,10 @@ llama_status llama_sync_status(llama_model* m, hipStream_t s) {
     if (flags) {
         HIP_TRY(hipMemset(m->deverr(), 0, sizeof flags));
         HIP_TRY(hipDeviceSynchronize());
-        return fail(LLAMA_ERR_INVALID_ARG, "device reported %s%s",
+        return fail(LLAMA_ERR_INVALID_ARG, "device reported %s%s%s",
                     (flags & DEVERR_TOKEN_RANGE) ? "token id outside [0, vocab) " : "",
-                    (flags & DEVERR_NAN_LOGIT) ? "NaN logits" : "");
+                    (flags & DEVERR_NAN_LOGIT) ? "NaN logits " : "",
+                    (flags & DEVERR_POSITION_RANGE) ? "position outside [0, max_seq)" : "");
     }
     return LLAMA_OK;
 }

@@ -17,13 +17,14 @@ __global__ __launch_bounds__(64) void attn_generic_kernel(const T* __restrict__ 
                                                            const T* __restrict__ vc,
                                                            T* __restrict__ out, int S,
                                                            int start_pos, const int* pos_dev,
+                                                           int pos_stride, int max_pos,
                                                            int H, int G, int d, int seq_stride,
                                                            float scale_log2, int out_pack) {
     const int row = blockIdx.x;  // b * S + s
     const int h = blockIdx.y;
     const int lane = threadIdx.x;
     const int b = row / S, s = row - b * S;
-    const int qpos = (pos_dev ? *pos_dev : start_pos) + s;
+    const int qpos = max(seq_pos(pos_dev, pos_stride, b, start_pos, max_pos), 0) + s;
     const int g = h / (H / G);
     __shared__ float qs[256];
     const T* qr = q + (size_t)row * H * d + (size_t)h * d;
@@ -79,7 +80,8 @@ hipError_t launch_generic(const AttnArgs& a, hipStream_t s) {
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)a.d);
     dim3 grid(rows, a.H);
     attn_generic_kernel<T><<<grid, 64, 0, s>>>((const T*)a.q, (const T*)a.kc, (const T*)a.vc,
-                                               (T*)a.out, a.S, a.start_pos, a.pos_dev, a.H, a.G,
+                                               (T*)a.out, a.S, a.start_pos, a.pos_dev,
+                                               a.pos_stride, a.max_pos, a.H, a.G,
                                                a.d, a.seq_stride, scale_log2, a.out_pack);
     return hipGetLastError();
 }
@@ -362,12 +364,13 @@ constexpr int DEC_BLOCK = 64;  // keys per wave per iteration
 
 __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
-    float* __restrict__ part, int start_pos, const int* pos_dev, int H, int G, int seq_stride,
+    float* __restrict__ part, int start_pos, const int* pos_dev, int pos_stride, int max_pos,
+    int H, int G, int seq_stride,
     int chunk, int max_splits, float scale_log2) {
     __shared__ float sm_m[4][16], sm_l[4][16];
     __shared__ f32x4 sm_o[3][8][64];
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-    const int pos = pos_dev ? *pos_dev : start_pos;
+    const int pos = max(seq_pos(pos_dev, pos_stride, b, start_pos, max_pos), 0);
     const int ctx = pos + 1;
     const int c0 = split * chunk;
     if (c0 >= ctx) return;  // no cached key in this split; the merge skips it
@@ -499,13 +502,14 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
 template <typename T>
 __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const float* __restrict__ part,
                                                                 T* __restrict__ out, int start_pos,
-                                                                const int* pos_dev, int H,
+                                                                const int* pos_dev,
+                                                                int pos_stride, int max_pos, int H,
                                                                 int d, int max_splits, int chunk,
                                                                 int out_pack) {
     __shared__ float wts[128];
     __shared__ float red[2];
     const int h = blockIdx.x, b = blockIdx.y;
-    const int pos = pos_dev ? *pos_dev : start_pos;
+    const int pos = max(seq_pos(pos_dev, pos_stride, b, start_pos, max_pos), 0);
     const int nsplit = (pos + 1 + chunk - 1) / chunk;  // <= 128
     const float* pp = part + (size_t)(b * H + h) * max_splits * (d + 2);
     const int t = threadIdx.x;
@@ -556,11 +560,12 @@ hipError_t launch_decode_mfma(const AttnArgs& a, hipStream_t s) {
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_D);
     attn_decode_mfma_kernel<<<dim3(splits, a.G, a.B), 256, 0, s>>>(
         (const bf16*)a.q, (const bf16*)a.kc, (const bf16*)a.vc, a.partials, a.start_pos,
-        a.pos_dev, a.H, a.G, a.seq_stride, chunk, max_splits, scale_log2);
+        a.pos_dev, a.pos_stride, a.max_pos, a.H, a.G, a.seq_stride, chunk, max_splits, scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     attn_decode_merge_kernel<bf16><<<dim3(a.H, a.B), 128, 0, s>>>(
-        a.partials, (bf16*)a.out, a.start_pos, a.pos_dev, a.H, FA_D, max_splits, chunk, a.out_pack);
+        a.partials, (bf16*)a.out, a.start_pos, a.pos_dev, a.pos_stride, a.max_pos, a.H, FA_D,
+        max_splits, chunk, a.out_pack);
     return hipGetLastError();
 }
 

@@ -78,4 +78,4 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) {
 }
 
 // Device error flags, OR-ed into a word of the workspace and read by llama_sync_status.
-enum : uint32_t { DEVERR_TOKEN_RANGE = 1u, DEVERR_NAN_LOGIT = 2u };
+enum : uint32_t { DEVERR_TOKEN_RANGE = 1u, DEVERR_NAN_LOGIT = 2u, DEVERR_POSITION_RANGE = 4u };

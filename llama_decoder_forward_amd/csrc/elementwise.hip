@@ -243,6 +243,15 @@ hipError_t zero_bytes(void* p, size_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
+__global__ void check_positions_kernel(const int* pos, int B, int max_pos, uint32_t* err) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B && (pos[b] < 0 || pos[b] >= max_pos)) atomicOr(err, DEVERR_POSITION_RANGE);
+}
+hipError_t check_positions(const int* pos, int B, int max_pos, uint32_t* err, hipStream_t s) {
+    check_positions_kernel<<<(B + 255) / 256, 256, 0, s>>>(pos, B, max_pos, err);
+    return hipGetLastError();
+}
+
 __global__ void copy_tokens_kernel(const int* src, int* dst, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) dst[i] = src[i];

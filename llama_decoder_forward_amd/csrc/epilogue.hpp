@@ -32,6 +32,18 @@ __host__ __device__ __forceinline__ size_t act_offset(int m, int k, int ld, int 
     return ((blk * 4 + ((k >> 3) & 3)) * R + (m & (R - 1))) * 8 + (k & 7);
 }
 
+// Position of sequence b's first token in this call: start_pos, or read from device memory
+// as pos_dev[b * pos_stride] (stride 0: one position shared by every sequence).  A device
+// value outside [0, max_pos) gives -1: readers then use position 0 and the KV-cache writes
+// are skipped, so no access leaves the cache or the rotary table and no valid cache entry
+// is overwritten (a check kernel raises the call's error flag).
+__device__ __forceinline__ int seq_pos(const int* pos_dev, int pos_stride, int b, int start_pos,
+                                       int max_pos) {
+    if (!pos_dev) return start_pos;
+    const int p = pos_dev[b * pos_stride];
+    return (p >= 0 && p < max_pos) ? p : -1;
+}
+
 // Weight rows of a GEMM, possibly split over up to three matrices stacked along n
 // (Q, K and V projections share one GEMM: rows [0,end0) of p0, then p1, then p2).
 template <typename T>
@@ -92,11 +104,14 @@ struct EpiQKV {
     T* q; T* kc; T* vc;
     const float2* rope;
     int Nq, Nk, d, S, start_pos, G, seq_stride;
-    const int* pos_dev;  // if set, the start position is read from device memory
+    const int* pos_dev;  // if set, the start positions are read from device memory (seq_pos)
+    int pos_stride, max_pos;
 
     __device__ __forceinline__ void operator()(int m, int n, float v[4]) const {
         const int b = m / S;
-        const int pos = (pos_dev ? *pos_dev : start_pos) + (m - b * S);
+        const int p0 = seq_pos(pos_dev, pos_stride, b, start_pos, max_pos);
+        const bool write_cache = p0 >= 0;
+        const int pos = (p0 >= 0 ? p0 : 0) + (m - b * S);
         if (n < Nq + Nk) {
             const int j = (n < Nq ? n : n - Nq) % d;  // even; pairs (j, j+1), (j+2, j+3)
             const float2 cs0 = rope[(size_t)pos * (d / 2) + j / 2];
@@ -109,6 +124,7 @@ struct EpiQKV {
         }
         if (n < Nq) {
             store4(q + (size_t)m * Nq + n, v);
+        } else if (!write_cache) {
         } else if (n < Nq + Nk) {
             const int nk = n - Nq, g = nk / d, j = nk - g * d;
             store4(kc + (((size_t)b * G + g) * seq_stride + pos) * d + j, v);

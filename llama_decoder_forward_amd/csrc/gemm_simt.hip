@@ -89,7 +89,7 @@ hipError_t simt_swiglu(const GemmArgs<void>& g, void* out, int ld, hipStream_t s
 }
 hipError_t simt_qkv(const GemmArgs<void>& g, const EpiQKV<void>& e, hipStream_t s) {
     EpiQKV<float> ef{(float*)e.q, (float*)e.kc, (float*)e.vc, e.rope, e.Nq, e.Nk, e.d, e.S,
-                     e.start_pos, e.G, e.seq_stride, e.pos_dev};
+                     e.start_pos, e.G, e.seq_stride, e.pos_dev, e.pos_stride, e.max_pos};
     return launch<float, false>(g, ef, s);
 }
 

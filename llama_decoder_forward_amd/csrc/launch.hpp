@@ -24,6 +24,8 @@ hipError_t zero_u32(uint32_t* p, int n, hipStream_t s);
 hipError_t zero_bytes(void* p, size_t bytes, hipStream_t s);
 hipError_t copy_tokens(const int* src, int* dst, int n, hipStream_t s);
 hipError_t set_counters(int* pos, int pos_value, int* step, hipStream_t s);
+// raise DEVERR_POSITION_RANGE if some pos[b], b < B, lies outside [0, max_pos)
+hipError_t check_positions(const int* pos, int B, int max_pos, uint32_t* err, hipStream_t s);
 
 // ---- GEMMs: acc[m][n] = sum_k A[m][k] W[n][k]  (gemm_mfma.hip, gemm_simt.hip, gemm_skinny.hip)
 template <typename T> struct GemmArgs {
@@ -52,7 +54,8 @@ struct AttnArgs {
     void* out;       // [rows][H*d] in the activation layout act_offset(row, col, H*d, out_pack)
     int out_pack;
     int B, S, start_pos, H, G, d, seq_stride;
-    const int* pos_dev;
+    const int* pos_dev;  // per-sequence start positions in device memory (seq_pos) or NULL
+    int pos_stride, max_pos;
     float* partials; // decode split-K scratch
     int max_ctx;     // upper bound of start_pos + S (sizing of decode grids)
 };

@@ -286,6 +286,22 @@ def prefill_sequence(tokens: np.ndarray, weights, cfg, cache: SequenceCache,
     return head_logits(x[-1:], weights, cfg, bf16_points)[0]
 
 
+def prefill_sequence_at(tokens: np.ndarray, start_pos: int, weights, cfg, cache: SequenceCache,
+                        all_positions: bool = False, dtype=np.float64) -> np.ndarray:
+    """Continue one sequence with the tokens at positions start_pos..start_pos+S-1, the cache
+    already holding positions 0..start_pos-1 (chunked prefill).  The same steps as
+    prefill_sequence, with the layers run at those positions: each token attends to every
+    cached position up to its own (article, section 多头注意力, the causal mask; the
+    pre-allocated cache of the Hacker News thread).  Returns the logits of the last
+    position [V], or of every new position [S, V]."""
+    x = embed(tokens, weights, dtype)
+    for layer in range(cfg.n_layers):
+        x = layer_forward(x, weights, cfg, layer, cache, start_pos=start_pos)
+    if all_positions:
+        return head_logits(x, weights, cfg)
+    return head_logits(x[-1:], weights, cfg)[0]
+
+
 def decode_sequence_step(token: int, pos: int, weights, cfg, cache: SequenceCache,
                          dtype=np.float64) -> np.ndarray:
     """One KV-cache decode step: the single token at position ``pos`` attends to the cached

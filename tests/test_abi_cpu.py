@@ -124,6 +124,17 @@ def test_call_shape_and_capacity_errors_before_device_work(lib, handle):
     assert lib.llama_layer_forward(handle, 2, T, T, 1, 4, 0, None) == -1  # layer out of range
     assert lib.llama_layer_forward(handle, 0, T, T, 1, 4, 30, None) == -3
     assert lib.llama_layer_forward(handle, 0, T, T, 3, 1, 0, None) == -3
+    assert lib.llama_prefill_at(handle, T, 1, 4, 29, T, 0, None) == -3  # 29 + 4 > max_seq
+    assert lib.llama_prefill_at(handle, T, 1, 4, -1, T, 0, None) == -3
+    assert lib.llama_prefill_at(handle, T, 3, 4, 0, T, 0, None) == -3    # B > max_batch
+    assert lib.llama_prefill_at(handle, T, 1, 0, 4, T, 0, None) == -2
+    assert lib.llama_prefill_at(handle, T, 1, 4, 4, None, 0, None) == -1
+    assert lib.llama_decode_step_ragged(handle, T, 3, T, T, T, None) == -3  # B > max_batch
+    assert lib.llama_decode_step_ragged(handle, T, 0, T, T, T, None) == -2
+    assert lib.llama_decode_step_ragged(handle, T, 1, None, T, T, None) == -1
+    assert lib.llama_decode_step_ragged(handle, T, 1, T, T, None, None) == -1
+    assert "max_batch" in lib.llama_last_error().decode() or "NULL" in lib.llama_last_error().decode()
+    assert lib.llama_decode_step(handle, T, 3, 3, T, T, None) == -3
     assert "max_batch" in lib.llama_last_error().decode()
     assert lib.llama_sync_status(None, None) == -1
 

@@ -130,3 +130,54 @@ def test_full_32_layer_stack_prefill_and_decode():
     err_d = assert_rows_close(lg[:1], ref[0][-1:], tol, "decode logits, 32 layers")
     say(f"  GPU prefill vs float32: max {err_p.max():.3e}; decode: {err_d.max():.3e}")
     assert np.isfinite(full).all()
+
+
+def test_ragged_decode_8b_widths():
+    """8B widths, 1 layer: four sequences prefilled to 4096 positions, then decoded together at
+    positions 4095, 1, 2000 and 700 (per-sequence contexts from 2 to 4096 keys, so a different
+    number of decode splits per row) for 2 teacher-forced steps."""
+    say("8B widths, 1 layer, prefill 4 x 4096, ragged decode at 4095 / 1 / 2000 / 700")
+    spec = _spec(1)
+    B, S, steps = 4, 4096, 2
+    positions = (4095, 1, 2000, 700)
+    m, synth = build_model(spec, 16, max_batch=B, max_seq=S + steps, max_tokens=B * S, cache=False)
+    toks = syn.tokens(16, B, S, spec.vocab_size)
+    m.prefill(torch.from_numpy(toks).cuda())
+    W = _oracle_weights(synth, 1)
+    say("  oracle prefixes (float32)")
+    caches = []
+    for b, p in enumerate(positions):
+        c = O.SequenceCache(spec, S + steps, np.float32)
+        O.prefill_sequence_at(toks[b, :p], 0, W, spec, c, dtype=np.float32)
+        caches.append(c)
+    pos = np.array(positions, dtype=np.int32)
+    cur = np.array([toks[b, p] for b, p in enumerate(positions)], dtype=np.int32)
+    for k in range(steps):
+        ref = np.stack([O.decode_sequence_step(int(cur[b]), int(pos[b]), W, spec, caches[b],
+                                               np.float32) for b in range(B)])
+        nxt, lg = m.decode_step_ragged(torch.from_numpy(cur).cuda(), torch.from_numpy(pos).cuda())
+        lg = lg.cpu().numpy()
+        assert_rows_close(lg, ref, BF16_TOL, f"ragged step {k}")
+        check_argmax(nxt.cpu().numpy(), lg, ref, f"ragged step {k}")
+        cur = O.argmax(ref).astype(np.int32)
+        pos = pos + 1
+    m.sync_status()
+
+
+def test_chunked_prefill_8b_widths():
+    """8B widths, 2 layers: a 2048-token prefill as two 1024-token chunks (the second at
+    start_pos 1024, the benchmark's tile shapes at half the tokens) against the oracle's
+    logits at every position of the second chunk, row 0 of 2."""
+    say("8B widths, 2 layers, prefill 2 x (1024 + 1024) chunks, all positions of chunk 2")
+    spec = _spec(2)
+    m, synth = build_model(spec, 17, max_batch=2, max_seq=2048, max_tokens=2048, cache=False)
+    toks = syn.tokens(17, 2, 2048, spec.vocab_size)
+    m.prefill(torch.from_numpy(np.ascontiguousarray(toks[:, :1024])).cuda())
+    got = m.prefill(torch.from_numpy(np.ascontiguousarray(toks[:, 1024:])).cuda(),
+                    all_positions=True, start_pos=1024)[0].cpu().numpy()
+    m.sync_status()
+    del m
+    W = _oracle_weights(synth, 2)
+    say("  oracle (float32), row 0")
+    ref, _ = O.prefill(toks[:1], W, spec, all_positions=True, dtype=np.float32)
+    assert_rows_close(got, ref[0, 1024:], BF16_TOL, "chunk 2 logits")

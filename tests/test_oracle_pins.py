@@ -286,6 +286,35 @@ def test_chunked_prefill_equals_single_prefill():
     np.testing.assert_allclose(c2.k[0], c1.k[0], rtol=1e-12, atol=1e-13)
 
 
+def test_prefill_in_chunks_equals_one_prefill():
+    # prefill_sequence_at over the chunks [0,6), [6,11), [11,17) gives the all-position
+    # logits of one prefill of the 17 tokens, and the same cache.
+    cfg = syn.TINY
+    W = syn.FloatView(syn.SyntheticWeights(cfg, seed=4))
+    toks = syn.tokens(4, 1, 17, cfg.vocab_size)[0]
+    full, caches = O.prefill(toks[None], W, cfg, all_positions=True)
+    cache = O.SequenceCache(cfg, 17)
+    parts = [O.prefill_sequence_at(toks[a:b], a, W, cfg, cache, all_positions=True)
+             for a, b in ((0, 6), (6, 11), (11, 17))]
+    np.testing.assert_allclose(np.concatenate(parts), full[0], rtol=1e-12, atol=1e-12)
+    for l in range(cfg.n_layers):
+        np.testing.assert_allclose(cache.v[l], caches[0].v[l], rtol=1e-12, atol=1e-13)
+    last = O.prefill_sequence_at(toks[11:], 11, W, cfg, O.SequenceCache(cfg, 17))
+    assert last.shape == (cfg.vocab_size,)
+
+
+def test_ragged_decode_positions_reproduce_prefill():
+    # Rows decoding at different positions over a cache filled further than their position
+    # (the entries past it are ignored and overwritten) give the prefill logits there.
+    cfg = syn.TINY
+    W = syn.FloatView(syn.SyntheticWeights(cfg, seed=5))
+    toks = syn.tokens(5, 3, 13, cfg.vocab_size)
+    full, caches = O.prefill(toks, W, cfg, all_positions=True)
+    for b, pos in enumerate((4, 12, 9)):
+        lg = O.decode_sequence_step(int(toks[b, pos]), pos, W, cfg, caches[b])
+        np.testing.assert_allclose(lg, full[b, pos], rtol=1e-12, atol=1e-12)
+
+
 def test_batch_rows_are_independent():
     cfg = syn.TINY
     W = syn.FloatView(syn.SyntheticWeights(cfg, seed=3))
