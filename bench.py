@@ -316,8 +316,11 @@ def main() -> int:
         r_steps = 8 if args.profile_only else 32
         pos_dev = torch.tensor(rpos, dtype=torch.int32, device="cuda")
         cur = first.clone()
-        for _ in range(2):                                # warmup (rewrites the same entries)
-            m.decode_step_ragged(cur, pos_dev, want_logits=False)
+        for _ in range(2):    # warmup of the timed loop body, including the position update
+            cur, _ = m.decode_step_ragged(cur, pos_dev, want_logits=False)
+            pos_dev += 1
+        pos_dev -= 2
+        cur = first.clone()
         torch.cuda.synchronize()
         start.record(stream)
         for _ in range(r_steps):
