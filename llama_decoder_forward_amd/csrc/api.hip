@@ -34,7 +34,7 @@ size_t elem_size(const llama_config& c) { return c.dtype == LLAMA_BF16 ? 2 : 4; 
 
 // Workspace regions, in order, each 256-byte aligned.
 struct Layout {
-    size_t flags, rope, x, h, q, attn, g, logits, partials, tokbuf, argmax, total;
+    size_t flags, rope, x, h, q, attn, g, logits, partials, kpart, tokbuf, argmax, total;
 };
 
 constexpr int kDecodeChunk = 64;  // key positions per split of the decode attention
@@ -58,6 +58,8 @@ Layout layout_of(const llama_config& c) {
     L.g = take(arows * (size_t)c.ffn_hidden * es);
     L.logits = take((size_t)c.max_batch * c.vocab_size * 4);
     L.partials = take((size_t)c.max_batch * c.n_heads * splits * (c.head_dim + 2) * 4);
+    // split-K sums of the residual GEMMs on the few-row path (at most 64 rows)
+    L.kpart = take((size_t)lk::LLAMA_MAX_KSPLITS * 64 * D * 4);
     L.tokbuf = take((size_t)c.max_batch * 4);
     L.argmax = take(lk::argmax_scratch_bytes(c.max_batch, c.vocab_size));
     L.total = off;
@@ -124,6 +126,7 @@ struct llama_model {
     void* g() { return ws + L.g; }
     float* logits_scratch() { return reinterpret_cast<float*>(ws + L.logits); }
     float* partials() { return reinterpret_cast<float*>(ws + L.partials); }
+    float* kpart() { return reinterpret_cast<float*>(ws + L.kpart); }
     int* tokbuf() { return reinterpret_cast<int*>(ws + L.tokbuf); }
     void* argmax_scratch() { return ws + L.argmax; }
     size_t kv_layer_elems() const {
@@ -192,10 +195,19 @@ lk::GemmArgs<void> gemm_args(llama_model* m, const void* A, int lda, const void*
     return g;
 }
 
+// Split-K sums of a residual GEMM not yet added to the residual stream (kpart, `splits`
+// slices of `stride` floats); the next RMSNorm of that stream adds them.
+struct Pending {
+    int splits = 0;
+    size_t stride = 0;
+};
+
 // One decoder layer on rows = B*S tokens (article, sections 构建Transformer层 to 前馈神经网络层).
+// pend, if given: on entry the sums pending on xin (then xin is written, folded), on return
+// those pending on xout.  Without it xout is complete on return.
 llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int B, int S,
                        int start_pos, const int* pos_dev, int pos_stride, int max_ctx, bool decode,
-                       hipStream_t s) {
+                       Pending* pend, hipStream_t s) {
     const llama_config& c = m->cfg;
     const llama_layer_weights& w = m->layers[l];
     const int T = B * S, D = c.dim, H = c.n_heads, G = c.n_kv_heads, d = c.head_dim;
@@ -208,7 +220,11 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
 
     {
         ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
-        HIP_TRY(lk::rmsnorm(m->dt, xin, 1, 0, w.attention_norm, m->h(), pk_qkv, T, D, c.norm_eps, s));
+        const Pending in = pend ? *pend : Pending{};
+        // pending sums exist only on the library's own residual buffer, which is writable
+        HIP_TRY(lk::rmsnorm_fold(m->dt, xin, m->kpart(), in.splits, in.stride,
+                                 const_cast<float*>(xin), 1, 0, w.attention_norm, m->h(), pk_qkv,
+                                 T, D, c.norm_eps, s));
     }
 
     lk::GemmArgs<void> qkv = gemm_args(m, m->h(), D, w.wq, T, Nq + 2 * Nk, D);
@@ -227,14 +243,21 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
         if (decode) HIP_TRY(lk::attention_decode(m->dt, aa, s));
         else HIP_TRY(lk::attention_prefill(m->dt, aa, s));
     }
+    // WO: x_out = x_in + attn WO, added by the FFN RMSNorm when split over K
+    const int wo_splits = lk::residual_splits(m->dt, T, D, Nq);
     {
         ProfScope ps(m, LLAMA_KERNEL_WO, s);
-        HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m, m->attn(), Nq, w.wo, T, D, Nq),
-                                  EpiResidual{xin, xout, D}, s));
+        const lk::GemmArgs<void> ga = gemm_args(m, m->attn(), Nq, w.wo, T, D, Nq);
+        if (wo_splits > 0) HIP_TRY(lk::gemm_residual_split(m->dt, ga, m->kpart(), wo_splits, s));
+        else HIP_TRY(lk::gemm_residual(m->dt, ga, EpiResidual{xin, xout, D}, s));
     }
     {
         ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
-        HIP_TRY(lk::rmsnorm(m->dt, xout, 1, 0, w.ffn_norm, m->h(), pk_up, T, D, c.norm_eps, s));
+        if (wo_splits > 0)
+            HIP_TRY(lk::rmsnorm_fold(m->dt, xin, m->kpart(), wo_splits, (size_t)T * D, xout, 1, 0,
+                                     w.ffn_norm, m->h(), pk_up, T, D, c.norm_eps, s));
+        else
+            HIP_TRY(lk::rmsnorm(m->dt, xout, 1, 0, w.ffn_norm, m->h(), pk_up, T, D, c.norm_eps, s));
     }
     lk::GemmArgs<void> ff = gemm_args(m, m->h(), D, w.w1, T, c.ffn_hidden, D);
     ff.W3 = WeightRows<void>{w.w3, w.w3, w.w3, c.ffn_hidden, c.ffn_hidden, D};
@@ -242,23 +265,30 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
         ProfScope ps(m, LLAMA_KERNEL_FFN_UP, s);
         HIP_TRY(lk::gemm_swiglu(m->dt, ff, m->g(), c.ffn_hidden, pk_down, s));
     }
+    // W2: x_out += g W2, left pending (split over K) when the caller takes pending sums
+    const int w2_splits = pend ? lk::residual_splits(m->dt, T, D, c.ffn_hidden) : 0;
     {
         ProfScope ps(m, LLAMA_KERNEL_FFN_DOWN, s);
-        HIP_TRY(lk::gemm_residual(m->dt, gemm_args(m, m->g(), c.ffn_hidden, w.w2, T, D, c.ffn_hidden),
-                                  EpiResidual{xout, xout, D}, s));
+        const lk::GemmArgs<void> ga = gemm_args(m, m->g(), c.ffn_hidden, w.w2, T, D, c.ffn_hidden);
+        if (w2_splits > 0) HIP_TRY(lk::gemm_residual_split(m->dt, ga, m->kpart(), w2_splits, s));
+        else HIP_TRY(lk::gemm_residual(m->dt, ga, EpiResidual{xout, xout, D}, s));
     }
+    if (pend) *pend = Pending{w2_splits, (size_t)T * D};
     return LLAMA_OK;
 }
 
 // Final RMSNorm and vocabulary projection of `rows` rows of x taken every `step` rows
 // starting at `offset` (article, section 预测下一个输出).
-llama_status run_head(llama_model* m, int rows, int step, int offset, float* logits, hipStream_t s) {
+// `pend`: split-K sums still pending on x (added to the rows read).
+llama_status run_head(llama_model* m, int rows, int step, int offset, const Pending& pend,
+                      float* logits, hipStream_t s) {
     const llama_config& c = m->cfg;
     {
         ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
-        HIP_TRY(lk::rmsnorm(m->dt, m->x(), step, offset, m->norm, m->h(),
-                            lk::act_pack(m->dt, rows, c.vocab_size, c.dim), rows, c.dim,
-                            c.norm_eps, s));
+        HIP_TRY(lk::rmsnorm_fold(m->dt, m->x(), m->kpart(), pend.splits, pend.stride, m->x(), step,
+                                 offset, m->norm, m->h(),
+                                 lk::act_pack(m->dt, rows, c.vocab_size, c.dim), rows, c.dim,
+                                 c.norm_eps, s));
     }
     {
         ProfScope ps(m, LLAMA_KERNEL_LM_HEAD, s);
@@ -275,13 +305,14 @@ llama_status run_decode_step(llama_model* m, const int32_t* tokens, int B, int p
                              int32_t* log_out, const int* step_ctr, hipStream_t s) {
     const llama_config& c = m->cfg;
     HIP_TRY(lk::embed(m->dt, tokens, m->tok_embeddings, m->x(), B, c.dim, c.vocab_size, m->deverr(), s));
+    Pending pend;
     for (int l = 0; l < c.n_layers; ++l) {
-        llama_status st =
-            run_layer(m, l, m->x(), m->x(), B, 1, pos, pos_dev, pos_stride, max_ctx, true, s);
+        llama_status st = run_layer(m, l, m->x(), m->x(), B, 1, pos, pos_dev, pos_stride, max_ctx,
+                                    true, &pend, s);
         if (st != LLAMA_OK) return st;
     }
     float* lg = logits ? logits : m->logits_scratch();
-    llama_status st = run_head(m, B, 1, 0, lg, s);
+    llama_status st = run_head(m, B, 1, 0, pend, lg, s);
     if (st != LLAMA_OK) return st;
     HIP_TRY(lk::argmax(lg, B, c.vocab_size, next, log_out, B, step_ctr, m->argmax_scratch(),
                        m->deverr(), s));
@@ -357,12 +388,14 @@ llama_status llama_prefill_at(llama_model* m, const int32_t* tokens, int32_t B, 
     if (st != LLAMA_OK) return st;
     const int T = B * S;
     HIP_TRY(lk::embed(m->dt, tokens, m->tok_embeddings, m->x(), T, c.dim, c.vocab_size, m->deverr(), s));
+    Pending pend;
     for (int l = 0; l < c.n_layers; ++l) {
-        st = run_layer(m, l, m->x(), m->x(), B, S, start_pos, nullptr, 0, start_pos + S, false, s);
+        st = run_layer(m, l, m->x(), m->x(), B, S, start_pos, nullptr, 0, start_pos + S, false,
+                       &pend, s);
         if (st != LLAMA_OK) return st;
     }
-    if (all_positions) return run_head(m, T, 1, 0, logits, s);
-    return run_head(m, B, S, S - 1, logits, s);
+    if (all_positions) return run_head(m, T, 1, 0, pend, logits, s);
+    return run_head(m, B, S, S - 1, pend, logits, s);
 }
 
 llama_status llama_prefill(llama_model* m, const int32_t* tokens, int32_t B, int32_t S,
@@ -440,7 +473,8 @@ llama_status llama_layer_forward(llama_model* m, int32_t layer, const float* x_i
         return fail(LLAMA_ERR_CAPACITY, "B*S=%lld > max_tokens=%d", (long long)B * S, c.max_tokens);
     llama_status st = ensure_rope(m, s);
     if (st != LLAMA_OK) return st;
-    return run_layer(m, layer, x_in, x_out, B, S, start_pos, nullptr, 0, start_pos + S, false, s);
+    return run_layer(m, layer, x_in, x_out, B, S, start_pos, nullptr, 0, start_pos + S, false,
+                     nullptr, s);
 }
 
 llama_status llama_sync_status(llama_model* m, hipStream_t s) {

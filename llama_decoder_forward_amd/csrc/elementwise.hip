@@ -54,12 +54,17 @@ hipError_t embed(Dt dt, const int* tokens, const void* E, float* x, int rows, in
 // y = x * 1/sqrt(mean(x^2) + eps) * w per row (article, section 分词器与编码; also the
 // pitchhut deep-dive's layer-normalisation example).  One 256-thread block per row; the
 // row lives in registers between the two passes.  D % 8 == 0, D <= 256*8*MAXV.
+//
+// With nsplit > 0 the row first takes the pending split-K sums of the residual GEMM that
+// wrote it: x' = x + parts[0] + parts[1] + ... (in that order), stored to x_out.
 template <typename T, int MAXV>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int in_step, int in_off,
                                                       const T* w, T* y, int y_pack, int D,
-                                                      float eps) {
+                                                      float eps, const float* parts, int nsplit,
+                                                      size_t split_stride, float* x_out) {
     const int r = blockIdx.x;
-    const float* xr = x + ((size_t)r * in_step + in_off) * D;
+    const size_t row = ((size_t)r * in_step + in_off) * D;
+    const float* xr = x + row;
     float v[MAXV][8];
     float ss = 0.0f;
 #pragma unroll
@@ -70,9 +75,38 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int in_ste
             const f32x4 b = *reinterpret_cast<const f32x4*>(xr + i + 4);
             v[c][0] = a[0]; v[c][1] = a[1]; v[c][2] = a[2]; v[c][3] = a[3];
             v[c][4] = b[0]; v[c][5] = b[1]; v[c][6] = b[2]; v[c][7] = b[3];
+            // splits in groups of four, each group's loads issued together (indices past
+            // the last split re-read it and are not added)
+            for (int z0 = 0; z0 < nsplit; z0 += 4) {
+                f32x4 pa[4], pb[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int z = z0 + u < nsplit ? z0 + u : nsplit - 1;
+                    const float* pr = parts + z * split_stride + row + i;
+                    pa[u] = *reinterpret_cast<const f32x4*>(pr);
+                    pb[u] = *reinterpret_cast<const f32x4*>(pr + 4);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (z0 + u < nsplit) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) { v[c][j] += pa[u][j]; v[c][4 + j] += pb[u][j]; }
+                    }
+            }
+            if (nsplit > 0) {
+                store4(x_out + row + i, v[c]);
+                store4(x_out + row + i + 4, v[c] + 4);
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) ss += v[c][j] * v[c][j];
         }
+    }
+    // the weights do not depend on the sum: load them before the block-wide reduction
+    float wv[MAXV][8];
+#pragma unroll
+    for (int c = 0; c < MAXV; ++c) {
+        const int i = (threadIdx.x + c * 256) * 8;
+        if (i < D) load8(w + i, wv[c]);
     }
     __shared__ float red[4];
     ss = wave_sum(ss);
@@ -84,11 +118,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int in_ste
     for (int c = 0; c < MAXV; ++c) {
         const int i = (threadIdx.x + c * 256) * 8;
         if (i < D) {
-            float wv[8];
-            load8(w + i, wv);
             float o[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o[j] = (v[c][j] * inv) * wv[j];
+            for (int j = 0; j < 8; ++j) o[j] = (v[c][j] * inv) * wv[c][j];
             T* yr = y + act_offset(r, i, D, y_pack);  // 8 consecutive values stay contiguous
             store4(yr, o);
             store4(yr + 4, o + 4);
@@ -98,26 +130,35 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int in_ste
 
 template <typename T>
 static hipError_t rmsnorm_t(const float* x, int step, int off, const T* w, T* y, int y_pack,
-                            int rows, int D, float eps, hipStream_t s) {
-    if (D <= 2048)
-        rmsnorm_kernel<T, 1><<<rows, 256, 0, s>>>(x, step, off, w, y, y_pack, D, eps);
-    else if (D <= 4096)
-        rmsnorm_kernel<T, 2><<<rows, 256, 0, s>>>(x, step, off, w, y, y_pack, D, eps);
-    else if (D <= 8192)
-        rmsnorm_kernel<T, 4><<<rows, 256, 0, s>>>(x, step, off, w, y, y_pack, D, eps);
-    else
-        rmsnorm_kernel<T, 8><<<rows, 256, 0, s>>>(x, step, off, w, y, y_pack, D, eps);
+                            int rows, int D, float eps, const float* parts, int nsplit,
+                            size_t split_stride, float* x_out, hipStream_t s) {
+#define LK_RMSNORM(V)                                                                         \
+    rmsnorm_kernel<T, V><<<rows, 256, 0, s>>>(x, step, off, w, y, y_pack, D, eps, parts, nsplit, \
+                                              split_stride, x_out)
+    if (D <= 2048) LK_RMSNORM(1);
+    else if (D <= 4096) LK_RMSNORM(2);
+    else if (D <= 8192) LK_RMSNORM(4);
+    else LK_RMSNORM(8);
+#undef LK_RMSNORM
     return hipGetLastError();
+}
+
+hipError_t rmsnorm_fold(Dt dt, const float* x, const float* parts, int nsplit, size_t split_stride,
+                        float* x_out, int in_row_step, int in_row_offset, const void* w, void* y,
+                        int y_pack, int rows, int D, float eps, hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    if (nsplit < 0 || (nsplit > 0 && (!parts || !x_out))) return hipErrorInvalidValue;
+    if (dt == Dt::BF16)
+        return rmsnorm_t<bf16>(x, in_row_step, in_row_offset, (const bf16*)w, (bf16*)y, y_pack, rows,
+                               D, eps, parts, nsplit, split_stride, x_out, s);
+    return rmsnorm_t<float>(x, in_row_step, in_row_offset, (const float*)w, (float*)y, y_pack, rows,
+                            D, eps, parts, nsplit, split_stride, x_out, s);
 }
 
 hipError_t rmsnorm(Dt dt, const float* x, int in_row_step, int in_row_offset, const void* w,
                    void* y, int y_pack, int rows, int D, float eps, hipStream_t s) {
-    if (rows == 0) return hipSuccess;
-    if (dt == Dt::BF16)
-        return rmsnorm_t<bf16>(x, in_row_step, in_row_offset, (const bf16*)w, (bf16*)y, y_pack, rows,
-                               D, eps, s);
-    return rmsnorm_t<float>(x, in_row_step, in_row_offset, (const float*)w, (float*)y, y_pack, rows,
-                            D, eps, s);
+    return rmsnorm_fold(dt, x, nullptr, 0, 0, nullptr, in_row_step, in_row_offset, w, y, y_pack,
+                        rows, D, eps, s);
 }
 
 // Greedy choice per row: the largest logit, lowest index among equals (article, section

@@ -77,6 +77,15 @@ struct EpiResidual {
     }
 };
 
+// One K split of a residual GEMM (split z = blockIdx.y): part[z][m][n] = the split's sum.
+// The RMSNorm that next reads the residual stream adds the splits in order z = 0, 1, ...
+struct EpiPartial {
+    float* part; int ld; size_t split_stride;
+    __device__ __forceinline__ void operator()(int m, int n, float v[4]) const {
+        store4(part + blockIdx.y * split_stride + (size_t)m * ld + n, v);
+    }
+};
+
 // SwiGLU gate (article, section 前馈神经网络层): g[m][n] = silu(h.w1_n) * (h.w3_n),
 // silu(z) = z / (1 + exp(-z)).
 // g is stored in the activation layout of the down projection (act_offset, pack).

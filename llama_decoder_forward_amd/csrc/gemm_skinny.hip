@@ -23,7 +23,7 @@ namespace {
 constexpr int SK_ROWS = 16;  // weight rows per strip
 constexpr int SK_KB = 128;   // k per block
 
-template <int NW, int RT, int MB, bool DUAL, typename Epi>
+template <int NW, int RT, int MB, bool DUAL, int BUDGET, typename Epi>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     const bf16* __restrict__ A, int pack, WeightRows<bf16> W, WeightRows<bf16> W3, int M, int N,
     int K, Epi epi) {
@@ -54,16 +54,19 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
             acc[r][mb] = f32x4{};
             if constexpr (DUAL) acc3[r][mb] = f32x4{};
         }
-    // this wave's share of the k blocks
+    // this wave's share of the k blocks: split blockIdx.y of gridDim.y takes a contiguous
+    // range of blocks, its NW waves divide that range
     const int blocks = K / SK_KB;
-    const int per = (blocks + NW - 1) / NW;
-    const int kb0 = wave * per;
-    const int kb1 = min(blocks, kb0 + per);
+    const int bps = (blocks + gridDim.y - 1) / gridDim.y;
+    const int sb0 = min(blocks, (int)blockIdx.y * bps), sb1 = min(blocks, sb0 + bps);
+    const int per = (sb1 - sb0 + NW - 1) / NW;
+    const int kb0 = sb0 + wave * per;
+    const int kb1 = min(sb1, kb0 + per);
 
-    // register stages: as many blocks in flight as about 96 VGPRs hold (a block takes 16
+    // register stages: as many blocks in flight as BUDGET VGPRs hold (a block takes 16
     // VGPRs per weight tile and per activation row block).  Deeper pipelines cost more in
     // occupancy than they gain (measured on MI355X, batch 1 to 64).
-    constexpr int NS0 = 96 / ((RT * NA + MB) * 16);
+    constexpr int NS0 = BUDGET / ((RT * NA + MB) * 16);
     constexpr int NS = NS0 < 1 ? 1 : NS0 > 4 ? 4 : NS0;
     u32x4 w[NS][RT][4], w3[NS][DUAL ? RT : 1][4], a[NS][MB][4];
     auto load = [&](int st, int kb) {
@@ -157,19 +160,49 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
         }
 }
 
+WeightRows<bf16> bf16_rows(const WeightRows<void>& w) {
+    return WeightRows<bf16>{(const bf16*)w.p0, (const bf16*)w.p1, (const bf16*)w.p2, w.end0, w.end1, w.ld};
+}
+
 template <int RT, int MB, bool DUAL, typename Epi>
 hipError_t launch_mb(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
-    const WeightRows<bf16> W{(const bf16*)g.W.p0, (const bf16*)g.W.p1, (const bf16*)g.W.p2, g.W.end0, g.W.end1, g.W.ld};
-    const WeightRows<bf16> W3{(const bf16*)g.W3.p0, (const bf16*)g.W3.p1, (const bf16*)g.W3.p2, g.W3.end0, g.W3.end1, g.W3.ld};
+    const WeightRows<bf16> W = bf16_rows(g.W), W3 = bf16_rows(g.W3);
     const int strips = g.N / (SK_ROWS * RT);
     const bf16* A = (const bf16*)g.A;
     // waves per strip: enough waves in flight to cover HBM latency (about 2-4k waves)
     if (strips >= 2048)
-        gemm_skinny_kernel<2, RT, MB, DUAL, Epi><<<strips, 128, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
+        gemm_skinny_kernel<2, RT, MB, DUAL, 96, Epi><<<strips, 128, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
     else if (strips >= 384)
-        gemm_skinny_kernel<4, RT, MB, DUAL, Epi><<<strips, 256, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
+        gemm_skinny_kernel<4, RT, MB, DUAL, 96, Epi><<<strips, 256, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
     else
-        gemm_skinny_kernel<8, RT, MB, DUAL, Epi><<<strips, 512, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
+        gemm_skinny_kernel<8, RT, MB, DUAL, 96, Epi><<<strips, 512, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
+    return hipGetLastError();
+}
+
+// Split-K layout of the residual GEMMs: strips of SPLIT_RT x 16 rows, `splits` k ranges of
+// NW waves, about LLAMA_SPLIT_TARGET_WGS workgroups (4 splits of 64 row strips for WO and
+// W2 of the 8B shape: 13 and 29 us at batch 32 against 17 and 39 us unsplit, on MI355X).
+#ifndef LLAMA_SPLIT_RT
+#define LLAMA_SPLIT_RT 4
+#endif
+#ifndef LLAMA_SPLIT_TARGET_WGS
+#define LLAMA_SPLIT_TARGET_WGS 256
+#endif
+#ifndef LLAMA_SPLIT_NW
+#define LLAMA_SPLIT_NW 8
+#endif
+#ifndef LLAMA_SPLIT_BUDGET
+#define LLAMA_SPLIT_BUDGET 96
+#endif
+constexpr int SPLIT_RT = LLAMA_SPLIT_RT;
+
+template <int MB>
+hipError_t launch_split(const GemmArgs<void>& g, float* part, int splits, hipStream_t s) {
+    const EpiPartial e{part, g.N, (size_t)g.M * g.N};
+    const dim3 grid(g.N / (SK_ROWS * SPLIT_RT), splits);
+    gemm_skinny_kernel<LLAMA_SPLIT_NW, SPLIT_RT, MB, false, LLAMA_SPLIT_BUDGET, EpiPartial>
+        <<<grid, LLAMA_SPLIT_NW * 64, 0, s>>>((const bf16*)g.A, g.a_pack, bf16_rows(g.W),
+                                              bf16_rows(g.W3), g.M, g.N, g.K, e);
     return hipGetLastError();
 }
 
@@ -180,6 +213,33 @@ int act_pack(Dt dt, int M, int N, int K) {
     int P = 1;
     while (P < M) P *= 2;
     return P;
+}
+
+// Activation fragments are loaded once per weight tile of a wave, so at batch 32 a wave with
+// one 16-row tile loads two bytes of activations per weight byte, and a compute unit streams
+// only about 36 GB/s of loads, cache hits included (measured on MI355X).  A residual GEMM with
+// few output rows (N = 4096) therefore gives each wave SPLIT_RT tiles and splits K over
+// workgroups instead, to keep every compute unit busy; the splits' sums go to `part` and
+// the next RMSNorm adds them to the residual stream.
+int residual_splits(Dt dt, int M, int N, int K) {
+    if (act_pack(dt, M, N, K) == 0 || N % (SK_ROWS * SPLIT_RT) != 0) return 0;
+    const int strips = N / (SK_ROWS * SPLIT_RT);
+    const int blocks = K / SK_KB;
+    int splits = (LLAMA_SPLIT_TARGET_WGS + strips - 1) / strips;
+    splits = splits < blocks ? splits : blocks;
+    splits = splits < LLAMA_MAX_KSPLITS ? splits : LLAMA_MAX_KSPLITS;
+    return splits >= 2 ? splits : 0;
+}
+
+hipError_t gemm_residual_split(Dt dt, const GemmArgs<void>& g, float* part, int splits,
+                               hipStream_t s) {
+    if (dt != Dt::BF16 || splits != residual_splits(dt, g.M, g.N, g.K) ||
+        g.a_pack != act_pack(dt, g.M, g.N, g.K))
+        return hipErrorInvalidValue;
+    const int mb = g.a_pack < 16 ? 1 : g.a_pack / 16;
+    if (mb == 1) return launch_split<1>(g, part, splits, s);
+    if (mb == 2) return launch_split<2>(g, part, splits, s);
+    return launch_split<4>(g, part, splits, s);
 }
 
 // Row tiles per wave (RT): every activation fragment serves RT weight tiles, which keeps the

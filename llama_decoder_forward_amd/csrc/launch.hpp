@@ -15,6 +15,12 @@ hipError_t embed(Dt dt, const int* tokens, const void* E, float* x, int rows, in
 // layout act_offset(r, i, D, y_pack)
 hipError_t rmsnorm(Dt dt, const float* x, int in_row_step, int in_row_offset, const void* w,
                    void* y, int y_pack, int rows, int D, float eps, hipStream_t s);
+// The same after folding pending split-K sums into the residual stream: for each row read,
+// x' = x + sum_z parts[z] (z = 0 .. nsplit-1 in order, split stride `split_stride` floats,
+// same row indexing as x) is written to x_out (may equal x) and normalised.
+hipError_t rmsnorm_fold(Dt dt, const float* x, const float* parts, int nsplit, size_t split_stride,
+                        float* x_out, int in_row_step, int in_row_offset, const void* w, void* y,
+                        int y_pack, int rows, int D, float eps, hipStream_t s);
 size_t argmax_scratch_bytes(int rows, int V);
 hipError_t argmax(const float* logits, int rows, int V, int* out, int* out2, int out2_step,
                   const int* counter, void* scratch, uint32_t* err, hipStream_t s);
@@ -43,6 +49,12 @@ template <bool DUAL, typename Epi>
 hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s);
 hipError_t gemm_store_f32(Dt dt, const GemmArgs<void>& g, EpiStoreF32 e, hipStream_t s);
 hipError_t gemm_residual(Dt dt, const GemmArgs<void>& g, EpiResidual e, hipStream_t s);
+// Split-K form of a residual GEMM on the weight-streaming path: part[z][m][n] (z < splits,
+// splits = residual_splits(...), split stride M*N floats) holds split z's share of acc; the
+// residual itself is not touched.  residual_splits returns 0 where this form is not used.
+constexpr int LLAMA_MAX_KSPLITS = 16;
+int residual_splits(Dt dt, int M, int N, int K);
+hipError_t gemm_residual_split(Dt dt, const GemmArgs<void>& g, float* part, int splits, hipStream_t s);
 hipError_t gemm_swiglu(Dt dt, const GemmArgs<void>& g, void* out, int ld, int out_pack, hipStream_t s);
 hipError_t gemm_qkv(Dt dt, const GemmArgs<void>& g, const EpiQKV<void>& e, hipStream_t s);
 
