@@ -346,12 +346,13 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
 // ------------------------------------------------------------------------------------
 // Decode, bf16, head_dim 128: split-K over the cached context on the matrix cores.
 //
-// Workgroup = (split of the context, KV head g, sequence b), 4 waves.  Each iteration the
+// Workgroup = (split of the context, KV head g, sequence b), NWV waves.  Each iteration the
 // waves take consecutive 64-key blocks and stream their K (16 KB) and V^T (16 KB) straight
 // from HBM into 16x16x32 MFMA operands, with the `group` query heads of g as the B-operand
 // columns (the rest zero): S^T = K Q^T, an online softmax per head, O^T += V^T P^T.  The
-// four waves' states are merged through LDS and one partial (max, sum, unnormalised o[128])
-// per query head is written; a second kernel merges the splits.
+// waves' states are merged through LDS.  With one split (enough (b, g) pairs to fill the
+// chip) the workgroup writes the attention output itself; otherwise it writes one partial
+// (max, sum, unnormalised o[128]) per query head and a second kernel merges the splits.
 //
 // Index maps (all 16-byte loads): lane (c = l%16, kq = l/16).  K tile t = 2j + h of a
 // 64-key block holds in MFMA row i the key 32j + 8(i/4) + 4h + i%4, so that the result
@@ -362,13 +363,14 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
 // ------------------------------------------------------------------------------------
 constexpr int DEC_BLOCK = 64;  // keys per wave per iteration
 
-__global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
+template <int NWV>
+__global__ __launch_bounds__(NWV * 64) void attn_decode_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
-    float* __restrict__ part, int start_pos, const int* pos_dev, int pos_stride, int max_pos,
-    int H, int G, int seq_stride,
+    float* __restrict__ part, bf16* __restrict__ out, int out_pack, int start_pos,
+    const int* pos_dev, int pos_stride, int max_pos, int H, int G, int seq_stride,
     int chunk, int max_splits, float scale_log2) {
-    __shared__ float sm_m[4][16], sm_l[4][16];
-    __shared__ f32x4 sm_o[3][8][64];
+    __shared__ float sm_m[NWV][16], sm_l[NWV][16];
+    __shared__ f32x4 sm_o[NWV - 1][8][64];
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int pos = max(seq_pos(pos_dev, pos_stride, b, start_pos, max_pos), 0);
     const int ctx = pos + 1;
@@ -395,7 +397,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4{};
 
-    for (int kb = c0 + wave * DEC_BLOCK; kb < c1; kb += 4 * DEC_BLOCK) {
+    for (int kb = c0 + wave * DEC_BLOCK; kb < c1; kb += NWV * DEC_BLOCK) {
         u32x4 kr[4][4], vr[8][2];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -469,7 +471,7 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
         }
     }
 
-    // merge the four waves (a wave with no key keeps m = -inf, l = 0, o = 0)
+    // merge the waves (a wave with no key keeps m = -inf, l = 0, o = 0)
     if (kq == 0) { sm_m[wave][col] = m_run; sm_l[wave][col] = l_run; }
     if (wave > 0) {
 #pragma unroll
@@ -479,21 +481,34 @@ __global__ __launch_bounds__(256) void attn_decode_mfma_kernel(
     if (wave > 0 || col >= group) return;
     float M = sm_m[0][col];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, sm_m[w][col]);
-    float wsc[4], L = 0.0f;
+    for (int w = 1; w < NWV; ++w) M = fmaxf(M, sm_m[w][col]);
+    float wsc[NWV], L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NWV; ++w) {
         wsc[w] = (sm_m[w][col] == -INFINITY) ? 0.0f : exp2f(sm_m[w][col] - M);
         L += wsc[w] * sm_l[w][col];
     }
     const int h = g * group + col;
+    if (gridDim.x == 1) {
+        // the whole context in this workgroup: o / l is the attention output
+        const float inv = 1.0f / L;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            f32x4 o = oacc[dt] * wsc[0];
+#pragma unroll
+            for (int w = 1; w < NWV; ++w) o += sm_o[w - 1][dt][lane] * wsc[w];
+            const float v[4] = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+            store4(out + act_offset(b, h * FA_D + 16 * dt + 4 * kq, H * FA_D, out_pack), v);
+        }
+        return;
+    }
     float* pp = part + ((size_t)(b * H + h) * max_splits + split) * (FA_D + 2);
     if (kq == 0) { pp[0] = M; pp[1] = L; }
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
         f32x4 o = oacc[dt] * wsc[0];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) o += sm_o[w - 1][dt][lane] * wsc[w];
+        for (int w = 1; w < NWV; ++w) o += sm_o[w - 1][dt][lane] * wsc[w];
         *reinterpret_cast<f32x4*>(pp + 2 + 16 * dt + 4 * kq) = o;
     }
 }
@@ -537,12 +552,20 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const float* __r
     }
 }
 
-// keys per split: enough workgroups (about 1024) to keep every CU streaming, at most 128
-// splits for the merge
+// Grid of the decode attention.  Where the (sequence, KV head) pairs alone fill the chip,
+// one workgroup of 8 waves takes a pair's whole context and writes the output (no partials,
+// no merge kernel).  Otherwise the context is split: keys per split grow until there are
+// about LLAMA_DEC_TARGET_WGS workgroups of 4 waves, at most 128 splits for the merge.
 #ifndef LLAMA_DEC_TARGET_WGS
 #define LLAMA_DEC_TARGET_WGS 8192
 #endif
-int decode_chunk(const AttnArgs& a) {
+#ifndef LLAMA_DEC_DIRECT_MIN_PAIRS
+#define LLAMA_DEC_DIRECT_MIN_PAIRS 256
+#endif
+struct DecodeGrid { int waves, chunk, splits; };
+DecodeGrid decode_grid(const AttnArgs& a) {
+    // one split covers every position of the cache
+    if ((long long)a.B * a.G >= LLAMA_DEC_DIRECT_MIN_PAIRS) return {8, a.seq_stride, 1};
     int chunk = 4 * DEC_BLOCK;
     while (chunk < 16 * 4 * DEC_BLOCK) {
         const long long splits = (a.max_ctx + chunk - 1) / chunk;
@@ -550,22 +573,29 @@ int decode_chunk(const AttnArgs& a) {
         chunk *= 2;
     }
     while ((a.max_ctx + chunk - 1) / chunk > 128) chunk *= 2;
-    return chunk;
+    return {4, chunk, (a.max_ctx + chunk - 1) / chunk};
 }
 
 hipError_t launch_decode_mfma(const AttnArgs& a, hipStream_t s) {
-    const int chunk = decode_chunk(a);
-    const int splits = (a.max_ctx + chunk - 1) / chunk;
+    const DecodeGrid dg = decode_grid(a);
     const int max_splits = (a.seq_stride + 4 * DEC_BLOCK - 1) / (4 * DEC_BLOCK);
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_D);
-    attn_decode_mfma_kernel<<<dim3(splits, a.G, a.B), 256, 0, s>>>(
-        (const bf16*)a.q, (const bf16*)a.kc, (const bf16*)a.vc, a.partials, a.start_pos,
-        a.pos_dev, a.pos_stride, a.max_pos, a.H, a.G, a.seq_stride, chunk, max_splits, scale_log2);
+    const dim3 grid(dg.splits, a.G, a.B);
+    if (dg.waves == 8)
+        attn_decode_mfma_kernel<8><<<grid, 512, 0, s>>>(
+            (const bf16*)a.q, (const bf16*)a.kc, (const bf16*)a.vc, a.partials, (bf16*)a.out,
+            a.out_pack, a.start_pos, a.pos_dev, a.pos_stride, a.max_pos, a.H, a.G, a.seq_stride,
+            dg.chunk, max_splits, scale_log2);
+    else
+        attn_decode_mfma_kernel<4><<<grid, 256, 0, s>>>(
+            (const bf16*)a.q, (const bf16*)a.kc, (const bf16*)a.vc, a.partials, (bf16*)a.out,
+            a.out_pack, a.start_pos, a.pos_dev, a.pos_stride, a.max_pos, a.H, a.G, a.seq_stride,
+            dg.chunk, max_splits, scale_log2);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || dg.splits == 1) return e;
     attn_decode_merge_kernel<bf16><<<dim3(a.H, a.B), 128, 0, s>>>(
         a.partials, (bf16*)a.out, a.start_pos, a.pos_dev, a.pos_stride, a.max_pos, a.H, FA_D,
-        max_splits, chunk, a.out_pack);
+        max_splits, dg.chunk, a.out_pack);
     return hipGetLastError();
 }
 

@@ -164,6 +164,49 @@ def test_ragged_decode_8b_widths():
     m.sync_status()
 
 
+def test_ragged_decode_batch32_whole_context_workgroups():
+    """8B widths, 1 layer, batch 32: the 32 x 8 (sequence, KV head) pairs fill the chip, so
+    each decode attention workgroup takes one pair's whole context and writes the output
+    itself (no split partials).  Rows decode at positions 1023, 0, 1, 63, 64, 65 and 511
+    (contexts of 1 to 1024 keys, so some of a workgroup's waves find no key and block ends
+    fall inside and at the edge of a 64-key block) and at seeded positions below 1024 for the
+    other 25; the first seven are checked against the oracle for 2 teacher-forced steps."""
+    say("8B widths, 1 layer, prefill 32 x 1024, ragged decode at 1023/0/1/63/64/65/511 + 25 more")
+    spec = _spec(1)
+    B, S, steps = 32, 1024, 2
+    checked = (1023, 0, 1, 63, 64, 65, 511)
+    rng = np.random.default_rng(18)
+    positions = np.concatenate([checked, rng.integers(0, S, B - len(checked))]).astype(np.int32)
+    m, synth = build_model(spec, 18, max_batch=B, max_seq=S + steps, max_tokens=B * S, cache=False)
+    toks = syn.tokens(18, B, S, spec.vocab_size)
+    m.prefill(torch.from_numpy(toks).cuda())
+    W = _oracle_weights(synth, 1)
+    say("  oracle prefixes (float32)")
+    caches = []
+    for b, p in enumerate(checked):
+        c = O.SequenceCache(spec, S + steps, np.float32)
+        if p > 0:
+            O.prefill_sequence_at(toks[b, :p], 0, W, spec, c, dtype=np.float32)
+        caches.append(c)
+    pos = positions.copy()
+    cur = np.array([toks[b, p] for b, p in enumerate(positions)], dtype=np.int32)
+    rows = list(range(len(checked)))
+    for k in range(steps):
+        ref = np.stack([O.decode_sequence_step(int(cur[b]), int(pos[b]), W, spec, caches[b],
+                                               np.float32) for b in rows])
+        nxt, lg = m.decode_step_ragged(torch.from_numpy(cur).cuda(), torch.from_numpy(pos).cuda())
+        lg = lg.cpu().numpy()
+        nxt = nxt.cpu().numpy()
+        assert_rows_close(lg[rows], ref, BF16_TOL, f"ragged step {k}")
+        check_argmax(nxt[rows], lg[rows], ref, f"ragged step {k}")
+        np.testing.assert_array_equal(nxt, np.argmax(lg, axis=-1))
+        assert np.isfinite(lg).all()
+        cur = nxt.astype(np.int32)
+        cur[rows] = O.argmax(ref).astype(np.int32)
+        pos = pos + 1
+    m.sync_status()
+
+
 def test_chunked_prefill_8b_widths():
     """8B widths, 2 layers: a 2048-token prefill as two 1024-token chunks (the second at
     start_pos 1024, the benchmark's tile shapes at half the tokens) against the oracle's
