@@ -102,7 +102,8 @@ typedef struct llama_model llama_model; /* opaque handle */
 size_t llama_kv_cache_bytes(const llama_config *cfg);
 
 /* Bytes of device workspace the caller must provide for this config (activations of up
- * to max_tokens rows, attention partials, the RoPE table, device flags). */
+ * to max_tokens rows, attention partials, split-K sums of the few-row GEMMs, the RoPE
+ * table, device flags). */
 size_t llama_workspace_bytes(const llama_config *cfg);
 
 /* Validate cfg, borrow the weights, KV cache and workspace, and return a handle in *out.
