@@ -302,7 +302,7 @@ def main() -> int:
                         f"{dec_ctx} prefilled positions, {dec_steps} steps (llama_generate)",
             "hbm_gbs": dbytes / (dms * 1e-3) / 1e9,
             "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "roofline": {"kernel": "decode attention (split-K over the cache)", "bound": "hbm",
+            "roofline": {"kernel": "decode attention (one workgroup per sequence and KV head over its whole context)", "bound": "hbm",
                          "achieved": a_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": a_gbs / PEAK_HBM_GBS,
                          "traffic": measured_traffic("attention_decode"),

@@ -192,8 +192,12 @@ def test_bf16_chunked_layer_forward():
     W = syn.FloatView(synth)
     outs = []
     for a, b in ((0, 40), (40, 77), (77, 78)):
-        outs.append(m.layer_forward(0, torch.from_numpy(np.ascontiguousarray(x[:, a:b])).cuda(),
-                                    start_pos=a).cpu().numpy())
+        chunk = np.ascontiguousarray(x[:, a:b])
+        x_in = torch.from_numpy(chunk).cuda()
+        outs.append(m.layer_forward(0, x_in, start_pos=a).cpu().numpy())
+        # the layer reads x_in and writes only x_out (the 2-token chunk takes the few-row
+        # GEMMs, whose split-K sums are added into x_out by the FFN norm)
+        np.testing.assert_array_equal(x_in.cpu().numpy(), chunk)
     got = np.concatenate(outs, axis=1)
     for bidx in range(2):
         cache = O.SequenceCache(spec, 78)
