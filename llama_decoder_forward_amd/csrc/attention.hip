@@ -552,10 +552,15 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const float* __r
     }
 }
 
-// Grid of the decode attention.  Where the (sequence, KV head) pairs alone fill the chip,
-// one workgroup of 8 waves takes a pair's whole context and writes the output (no partials,
-// no merge kernel).  Otherwise the context is split: keys per split grow until there are
-// about LLAMA_DEC_TARGET_WGS workgroups of 4 waves, at most 128 splits for the merge.
+// Grid of the decode attention.  Where the (sequence, KV head) pairs alone fill the chip
+// and every sequence sits at the same position, one workgroup of 8 waves takes a pair's
+// whole context and writes the output (no partials, no merge kernel).  Otherwise the
+// context is split: keys per split grow until there are about LLAMA_DEC_TARGET_WGS
+// workgroups of 4 waves, at most 128 splits for the merge.  With a position per sequence
+// (ragged batches) whole-context workgroups would all wait on the longest context, and the
+// many small splits balance the CUs (measured on MI355X at batch 32 with contexts spread
+// over 2048..4096: 83 against 91 us on one machine, equal on another; the wider the spread,
+// the more the whole-context grid leaves idle).
 #ifndef LLAMA_DEC_TARGET_WGS
 #define LLAMA_DEC_TARGET_WGS 8192
 #endif
@@ -565,7 +570,8 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const float* __r
 struct DecodeGrid { int waves, chunk, splits; };
 DecodeGrid decode_grid(const AttnArgs& a) {
     // one split covers every position of the cache
-    if ((long long)a.B * a.G >= LLAMA_DEC_DIRECT_MIN_PAIRS) return {8, a.seq_stride, 1};
+    const bool ragged = a.pos_dev && a.pos_stride != 0;
+    if (!ragged && (long long)a.B * a.G >= LLAMA_DEC_DIRECT_MIN_PAIRS) return {8, a.seq_stride, 1};
     int chunk = 4 * DEC_BLOCK;
     while (chunk < 16 * 4 * DEC_BLOCK) {
         const long long splits = (a.max_ctx + chunk - 1) / chunk;
