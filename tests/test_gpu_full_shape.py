@@ -164,13 +164,12 @@ def test_ragged_decode_8b_widths():
     m.sync_status()
 
 
-def test_ragged_decode_batch32_whole_context_workgroups():
-    """8B widths, 1 layer, batch 32: the 32 x 8 (sequence, KV head) pairs fill the chip, so
-    each decode attention workgroup takes one pair's whole context and writes the output
-    itself (no split partials).  Rows decode at positions 1023, 0, 1, 63, 64, 65 and 511
-    (contexts of 1 to 1024 keys, so some of a workgroup's waves find no key and block ends
-    fall inside and at the edge of a 64-key block) and at seeded positions below 1024 for the
-    other 25; the first seven are checked against the oracle for 2 teacher-forced steps."""
+def test_ragged_decode_batch32():
+    """8B widths, 1 layer, batch 32 with a position per sequence (the split attention grid,
+    which balances the CUs over unequal contexts).  Rows decode at positions 1023, 0, 1, 63,
+    64, 65 and 511 (contexts of 1 to 1024 keys: splits with no key, and block ends inside and
+    at the edge of a 64-key block) and at seeded positions below 1024 for the other 25; the
+    first seven are checked against the oracle for 2 teacher-forced steps."""
     say("8B widths, 1 layer, prefill 32 x 1024, ragged decode at 1023/0/1/63/64/65/511 + 25 more")
     spec = _spec(1)
     B, S, steps = 32, 1024, 2
@@ -204,6 +203,48 @@ def test_ragged_decode_batch32_whole_context_workgroups():
         cur = nxt.astype(np.int32)
         cur[rows] = O.argmax(ref).astype(np.int32)
         pos = pos + 1
+    m.sync_status()
+
+
+def test_decode_batch32_whole_context_workgroups_short_contexts():
+    """8B widths, 1 layer, batch 32 at one position for all sequences: the 32 x 8
+    (sequence, KV head) pairs fill the chip, so each attention workgroup takes one pair's
+    whole context with 8 waves and writes the output itself.  Decode at position 0 into an
+    empty cache (one key: seven of the eight waves find none), then, after a 62-token
+    prefill, at positions 62..65 (the context crosses the edge of a 64-key block).  Rows 0
+    and 31 are checked against the oracle, teacher-forced."""
+    say("8B widths, 1 layer, batch 32: decode at 0, then prefill 62 and decode at 62..65")
+    spec = _spec(1)
+    B, S = 32, 62
+    m, synth = build_model(spec, 19, max_batch=B, max_seq=128, max_tokens=B * 64, cache=False)
+    toks = syn.tokens(19, B, 66, spec.vocab_size)
+    W = _oracle_weights(synth, 1)
+    rows = [0, 31]
+    nxt, lg = m.decode_step(torch.from_numpy(np.ascontiguousarray(toks[:, 0])).cuda(), 0)
+    ref = np.stack([O.decode_sequence_step(int(toks[b, 0]), 0, W, spec,
+                                           O.SequenceCache(spec, 128, np.float32), np.float32)
+                    for b in rows])
+    lg = lg.cpu().numpy()
+    assert_rows_close(lg[rows], ref, BF16_TOL, "decode at position 0")
+    check_argmax(nxt.cpu().numpy()[rows], lg[rows], ref, "decode at position 0")
+    m.prefill(torch.from_numpy(np.ascontiguousarray(toks[:, :S])).cuda())
+    caches = []
+    for b in rows:
+        c = O.SequenceCache(spec, 128, np.float32)
+        O.prefill_sequence_at(toks[b, :S], 0, W, spec, c, dtype=np.float32)
+        caches.append(c)
+    cur = np.ascontiguousarray(toks[:, S]).astype(np.int32)
+    for k in range(4):
+        ref = np.stack([O.decode_sequence_step(int(cur[b]), S + k, W, spec, caches[i], np.float32)
+                        for i, b in enumerate(rows)])
+        nxt, lg = m.decode_step(torch.from_numpy(cur).cuda(), S + k)
+        lg = lg.cpu().numpy()
+        nxt = nxt.cpu().numpy()
+        assert_rows_close(lg[rows], ref, BF16_TOL, f"decode at position {S + k}")
+        check_argmax(nxt[rows], lg[rows], ref, f"decode at position {S + k}")
+        assert np.isfinite(lg).all()
+        cur = nxt.astype(np.int32)
+        cur[rows] = O.argmax(ref).astype(np.int32)
     m.sync_status()
 
 
