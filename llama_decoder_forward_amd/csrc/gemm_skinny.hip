@@ -243,20 +243,30 @@ hipError_t gemm_residual_split(Dt dt, const GemmArgs<void>& g, float* part, int 
 }
 
 // Row tiles per wave (RT): every activation fragment serves RT weight tiles, which keeps the
-// L2 traffic for activations below the weight stream when the batch is 32 or more; but RT
-// also divides the number of waves, so it is used only where N leaves enough strips (the
-// vocabulary projection, the gate/up pair).  Measured on MI355X at batch 4 and 32.
+// L2 traffic for activations below the weight stream; but RT also divides the number of
+// waves, so it is used only where N leaves enough strips (the vocabulary projection, the
+// gate/up pair).  Measured on MI355X, 8B shape:
+//   - vocabulary projection: 1 row 197 -> 176 us with RT 4; batch 32 209 -> 197 us with RT 8
+//     (against RT 4);
+//   - gate/up pair: batch 4 50 -> 45 us with RT 2; batch 32 RT 2 (RT 4 no faster);
+//   - Q/K/V with RT 2 at batch 4: 17 -> 21 us, so RT 1.
 template <bool DUAL, typename Epi>
 hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     if (g.a_pack != act_pack(Dt::BF16, g.M, g.N, g.K)) return hipErrorInvalidValue;
     const int mb = g.a_pack < 16 ? 1 : g.a_pack / 16;  // 16-row MFMA column blocks
     const bool wide = g.N >= 16384;
-    if (mb == 1) return launch_mb<1, 1, DUAL>(g, e, s);
     if constexpr (DUAL) {
-        if (mb == 2 && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 2, DUAL>(g, e, s);
+        if (mb <= 2 && g.N % (SK_ROWS * 2) == 0) {
+            if (mb == 1) return launch_mb<2, 1, DUAL>(g, e, s);
+            return launch_mb<2, 2, DUAL>(g, e, s);
+        }
+        if (mb == 1) return launch_mb<1, 1, DUAL>(g, e, s);
         if (mb == 2) return launch_mb<1, 2, DUAL>(g, e, s);
         return launch_mb<1, 4, DUAL>(g, e, s);
     } else {
+        if (mb == 1 && wide && g.N % (SK_ROWS * 4) == 0) return launch_mb<4, 1, DUAL>(g, e, s);
+        if (mb == 1) return launch_mb<1, 1, DUAL>(g, e, s);
+        if (mb == 2 && wide && g.N % (SK_ROWS * 8) == 0) return launch_mb<8, 2, DUAL>(g, e, s);
         if (mb == 2 && wide && g.N % (SK_ROWS * 4) == 0) return launch_mb<4, 2, DUAL>(g, e, s);
         if (mb == 2) return launch_mb<1, 2, DUAL>(g, e, s);
         if (wide && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 4, DUAL>(g, e, s);
