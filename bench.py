@@ -177,7 +177,7 @@ def main() -> int:
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus must be 1)", file=sys.stderr, flush=True)
         return 2
 
