@@ -163,13 +163,16 @@ def main() -> int:
     ap.add_argument("--decode-ctx", type=int, default=4096)
     ap.add_argument("--seq", type=int, default=2048)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context leg (4 x 8192 prefill, then batch-4 decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
     ap.add_argument("--print-source-hash", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
-                    help="a short run for rocprofv3: 1 warmup + --steps prefill, 8 decode steps")
+                    help="a short run for rocprofv3: 1 warmup + --steps prefill, 8 decode steps, "
+                         "no long-context leg and no CPU baseline")
     args = ap.parse_args()
 
     if args.print_source_hash:
@@ -370,10 +373,58 @@ def main() -> int:
                 "tflops": cfl / (cms * 1e-3) / 1e12,
             }
 
+    # ---------------------------------------------------------------- long context
+    # 4 sequences of 8192 tokens prefilled in one call (timed), then 64 greedy decode steps
+    # of the batch against those caches (llama_generate, timed); a model of its own, with
+    # the cache sized for 8192 + 64 positions
+    if not args.no_long and not args.profile_only:
+        L_B, L_S, L_steps = 4, 8192, 64
+        del m
+        torch.cuda.empty_cache()
+        ml = bd.Model(spec, weights, max_batch=L_B, max_seq=L_S + L_steps, max_tokens=L_B * L_S)
+        ltoks = torch.from_numpy(syn.tokens(5, L_B, L_S, spec.vocab_size)).cuda()
+        lg = ml.prefill(ltoks)                            # warmup
+        torch.cuda.synchronize()
+        l_runs = 2
+        start.record(stream)
+        for _ in range(l_runs):
+            lg = ml.prefill(ltoks)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        lp_ms = start.elapsed_time(stop) / l_runs
+        first = lg.argmax(-1).to(torch.int32).contiguous()
+        ml.generate(first, L_S, L_steps)                  # warmup (same positions)
+        torch.cuda.synchronize()
+        start.record(stream)
+        ml.generate(first, L_S, L_steps)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ld_ms = start.elapsed_time(stop)
+        ml.sync_status()
+        lfl = prefill_flops(spec, L_B, L_S)
+        lbytes = decode_bytes(spec, L_B, L_S + 1, L_steps)
+        log(f"long context: prefill {lp_ms:.1f} ms, decode {ld_ms / L_steps:.3f} ms/step")
+        result["long_context"] = {
+            "workload": f"llama3-8b-shaped prefill of {L_B} x {L_S} tokens in one call, then "
+                        f"{L_steps} greedy decode steps of the batch (llama_generate)",
+            "prefill": {"value": L_B * L_S / (lp_ms * 1e-3), "unit": "tokens/s",
+                        "ms_per_step": lp_ms, "steps": l_runs,
+                        "mfma_frac": lfl / (lp_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "tflops": lfl / (lp_ms * 1e-3) / 1e12},
+            "decode": {"value": L_B * L_steps / (ld_ms * 1e-3), "unit": "tokens/s",
+                       "ms_per_step": ld_ms / L_steps, "steps": L_steps, "batch": L_B,
+                       "context": [L_S + 1, L_S + L_steps],
+                       "hbm_gbs": lbytes / (ld_ms * 1e-3) / 1e9,
+                       "hbm_frac": lbytes / (ld_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        }
+        del ml
+        m = None
+
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline and not args.profile_only:
         log("timing the CPU oracle sample")
-        del m, weights
+        m = None
+        del weights
         torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(spec, seed, S, args.cpu_layers)
     print(json.dumps(result), flush=True)

@@ -72,6 +72,12 @@ __device__ __forceinline__ void wait_vm_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
+// Wait for this wave's LDS operations, then synchronise the workgroup (outstanding global
+// loads stay in flight).
+__device__ __forceinline__ void wait_lgkm_and_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
 // LDS byte address of a __shared__ (address space 3) pointer, for the m0 of lds_dma16.
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
     return (unsigned)(uintptr_t)((__attribute__((address_space(3))) const void*)p);

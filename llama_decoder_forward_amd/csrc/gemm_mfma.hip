@@ -7,11 +7,15 @@
 // the RoPE pairs (2i, 2i+1) and the SwiGLU gate/up columns meet in one lane, and the
 // epilogue stores 8- or 16-byte vectors.
 //
-// Block tile BN (weight rows) x BM (tokens) x 64 (k), staged through LDS in two buffers,
-// 16-byte chunks XOR-swizzled by row (chunk c of row r at c ^ (r & 7)) so that the 32 lanes
-// of an MFMA operand read hit distinct banks.  Global loads of step k+1 are issued before
-// the MFMAs of step k.  Requires K % 64 == 0 and N % 4 == 0; M and N tails are masked.
+// Block tile BN (weight rows) x BM (tokens) x 64 (k), staged through two LDS buffers, 16-byte
+// chunks XOR-swizzled by row so that the 32 lanes of an MFMA operand read hit distinct banks.
+// The operand copies pass through registers: a tile is loaded from global memory two tiles
+// ahead of the MFMAs and written to LDS one tile ahead.  Requires K % 64 == 0 and N % 4 == 0;
+// M and N tails are masked.
 #include "launch.hpp"
+
+#include <type_traits>
+#include <utility>
 
 namespace lk {
 
@@ -22,11 +26,21 @@ hipError_t simt_qkv(const GemmArgs<void>& g, const EpiQKV<void>& e, hipStream_t 
 
 namespace {
 
-// Block tile BN weight rows x BM tokens x BK, STAGES-deep LDS ring; the grid covers weight
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Block tile BN weight rows x BM tokens x BK, two LDS buffers; the grid covers weight
 // rows [n_begin, N) and all M tokens.  LDS row = BK bf16
 // (RB bytes) split in 16-byte chunks; chunk c of row r is stored at c ^ swz(r) so that the
 // MFMA operand reads of consecutive rows hit distinct banks.
-template <int BN, int BM, int BK, int STAGES, int WN, int WM, bool DUAL, typename Epi>
+template <int BN, int BM, int BK, int WN, int WM, bool DUAL, typename Epi>
 __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
     const bf16* __restrict__ A, int lda, WeightRows<bf16> W, WeightRows<bf16> W3, int M, int N,
     int K, int n_begin, Epi epi) {
@@ -39,7 +53,6 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
     constexpr int SPW = STAGE / 1024 / NW;     // 1 KB copies per wave per stage
     constexpr int TN = BN / WN / 32, TM = BM / WM / 32;
     static_assert(STAGE % (1024 * NW) == 0, "stage must split into whole 1 KB copies per wave");
-    static_assert((STAGES - 2) * SPW < 64, "vmcnt range");
     extern __shared__ u32x4 lds[];
 
     // 8 consecutive rows (one 128-byte bank window) and 16 consecutive rows (a 256-byte one)
@@ -77,14 +90,6 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
         }
         src[i] = p + c * 8;
     }
-    // LDS byte offset of the ring (address-space cast from the generic pointer)
-    const unsigned lds0 = (unsigned)(uintptr_t)((__attribute__((address_space(3))) const void*)lds);
-    auto issue = [&](int st, int k0) {
-#pragma unroll
-        for (int i = 0; i < SPW; ++i)
-            lds_dma16(src[i] + k0, lds0 + st * STAGE + (wave + i * NW) * 1024);
-    };
-
     f32x16 acc[TN][TM];
     f32x16 acc3[DUAL ? TN : 1][DUAL ? TM : 1];
 #pragma unroll
@@ -97,51 +102,60 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
 
     const int lr = lane & 31, lh = lane >> 5;
     const int nk = K / BK;
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-        if (st < nk) issue(st, st * BK);
-
-    // The copies of tile kt + STAGES - 1 are spread over the k-steps of tile kt, a few
-    // behind each step's MFMAs: issued all at once, the 8 waves' copies queue up in the
-    // address unit and every wave stalls behind its own before reaching its MFMAs.
     constexpr int KSTEPS = BK / 16;
-    constexpr int PPS = (SPW + KSTEPS - 1) / KSTEPS;  // copies per k-step
-    auto issue_part = [&](int st, int k0, int kk) {
+    static_assert(KSTEPS % 2 == 0, "the fragment double buffer alternates per k-step");
+
+    // Copies go through registers: tile kt+1, loaded from global memory during tile kt-1,
+    // is written into the other LDS buffer over the first KSTEPS-1 k-steps of tile kt, and
+    // each write is followed by the load of the same share of tile kt+2 into the registers
+    // it frees.  The barrier after k-step KSTEPS-2 publishes tile kt+1 and ends every read
+    // of tile kt's buffer (the last k-step's fragments are in registers by then), so the
+    // last k-step's MFMAs run while the fragments of tile kt+1's first k-step are read.
+    constexpr int WSTEPS = KSTEPS - 1;
+    constexpr int WPS = (SPW + WSTEPS - 1) / WSTEPS;  // copies per k-step
+    u32x4 stg[SPW];
+    char* ldsb = reinterpret_cast<char*>(lds);
+    auto gload = [&](int i, int k0) { stg[i] = *reinterpret_cast<const u32x4*>(src[i] + k0); };
+    auto lwrite = [&](int st, int i) {
+        *reinterpret_cast<u32x4*>(ldsb + st * STAGE + (wave + i * NW) * 1024 + lane * 16) = stg[i];
+    };
+    bf16x8 fa[2][TN], fa3[2][DUAL ? TN : 1], fb[2][TM];
+    auto frags = [&](int buf, const char* base, int kk) {
+        const int ch = kk * 2 + lh;
 #pragma unroll
-        for (int q = 0; q < PPS; ++q) {
-            const int i = kk * PPS + q;
-            if (i < SPW) lds_dma16(src[i] + k0, lds0 + st * STAGE + (wave + i * NW) * 1024);
+        for (int i = 0; i < TN; ++i) {
+            const int r = wn * (BN / WN) + i * 32 + lr;
+            fa[buf][i] = *reinterpret_cast<const bf16x8*>(base + r * RB + (ch ^ swz(r)) * 16);
+            if constexpr (DUAL)
+                fa3[buf][i] = *reinterpret_cast<const bf16x8*>(base + (BN + r) * RB + (ch ^ swz(BN + r)) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+            const int r = NA * BN + wm * (BM / WM) + j * 32 + lr;
+            fb[buf][j] = *reinterpret_cast<const bf16x8*>(base + r * RB + (ch ^ swz(r)) * 16);
         }
     };
-    for (int kt = 0; kt < nk; ++kt) {
-        // tile kt has landed once at most the copies of the later tiles are outstanding
-        if (kt + STAGES - 2 < nk) wait_vm_and_barrier<(STAGES - 2) * SPW>();
-        else wait_vm_and_barrier<0>();
-        const bool more = kt + STAGES - 1 < nk;
-        const int nst = (kt + STAGES - 1) % STAGES, nk0 = (kt + STAGES - 1) * BK;
-        const char* base = reinterpret_cast<const char*>(lds) + (kt % STAGES) * STAGE;
-        // fragments of k-step kk+1 are read from LDS while the MFMAs of step kk run
-        bf16x8 fa[2][TN], fa3[2][DUAL ? TN : 1], fb[2][TM];
-        auto frags = [&](int buf, int kk) {
-            const int ch = kk * 2 + lh;
 #pragma unroll
-            for (int i = 0; i < TN; ++i) {
-                const int r = wn * (BN / WN) + i * 32 + lr;
-                fa[buf][i] = *reinterpret_cast<const bf16x8*>(base + r * RB + (ch ^ swz(r)) * 16);
-                if constexpr (DUAL)
-                    fa3[buf][i] = *reinterpret_cast<const bf16x8*>(base + (BN + r) * RB + (ch ^ swz(BN + r)) * 16);
-            }
+    for (int i = 0; i < SPW; ++i) gload(i, 0);
 #pragma unroll
-            for (int j = 0; j < TM; ++j) {
-                const int r = NA * BN + wm * (BM / WM) + j * 32 + lr;
-                fb[buf][j] = *reinterpret_cast<const bf16x8*>(base + r * RB + (ch ^ swz(r)) * 16);
-            }
-        };
-        frags(0, 0);
+    for (int i = 0; i < SPW; ++i) lwrite(0, i);
+    if (nk > 1) {
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-            const int cur = kk & 1;
-            if (kk + 1 < BK / 16) frags(cur ^ 1, kk + 1);
+        for (int i = 0; i < SPW; ++i) gload(i, BK);
+    }
+    wait_lgkm_and_barrier();
+    frags(0, ldsb, 0);
+    // WR: a tile kt+1 exists (write it, read its first fragments); LD: a tile kt+2 exists
+    auto tile = [&](int kt, auto wr_c, auto ld_c) {
+        constexpr bool WR = decltype(wr_c)::value, LD = decltype(ld_c)::value;
+        const char* base = ldsb + (kt & 1) * STAGE;
+        const char* nbase = ldsb + ((kt + 1) & 1) * STAGE;
+        const int wst = (kt + 1) & 1, k2 = (kt + 2) * BK;
+        static_for<KSTEPS>([&](auto kk_c) {
+            constexpr int kk = decltype(kk_c)::value;
+            constexpr int cur = kk & 1;
+            if constexpr (kk + 1 < KSTEPS) frags(cur ^ 1, base, kk + 1);
+            else if constexpr (WR) frags(cur ^ 1, nbase, 0);
 #pragma unroll
             for (int i = 0; i < TN; ++i)
 #pragma unroll
@@ -150,23 +164,50 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
                     if constexpr (DUAL)
                         acc3[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa3[cur][i], fb[cur][j], acc3[i][j], 0, 0, 0);
                 }
-            if (kk + 1 < BK / 16) {
-                // interleave: one LDS read after each MFMA, then the remaining MFMAs
-                constexpr int NREAD = NA * TN + TM, NMFMA = NA * TN * TM;
+            // one scheduling region per k-step: an LDS read after each of the first MFMAs,
+            // then one LDS write and one global load after each of the next ones
+            constexpr int NREAD = NA * TN + TM, NMFMA = NA * TN * TM;
+            constexpr int NWR = (WR && kk < WSTEPS) ? ((kk + 1) * WPS <= SPW ? WPS : SPW - kk * WPS) : 0;
+            constexpr int NRD = (kk + 1 < KSTEPS || WR) ? NREAD : 0;
+            if constexpr (NRD + NWR <= NMFMA) {
 #pragma unroll
-                for (int q = 0; q < NREAD; ++q) {
+                for (int q = 0; q < NRD; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
-            }
-            if (more) {
+#pragma unroll
+                for (int q = 0; q < NWR; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+                    if constexpr (LD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NRD - NWR, 0);
+            } else {
                 __builtin_amdgcn_sched_barrier(0);
-                issue_part(nst, nk0, kk);
-                __builtin_amdgcn_sched_barrier(0);
             }
-        }
+            if constexpr (WR) {
+                if (kk < WSTEPS) {
+#pragma unroll
+                    for (int q = 0; q < WPS; ++q) {
+                        const int i = kk * WPS + q;
+                        if (i < SPW) {
+                            lwrite(wst, i);
+                            if constexpr (LD) gload(i, k2);
+                        }
+                    }
+                }
+            }
+            if constexpr (kk == KSTEPS - 2) wait_lgkm_and_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) tile(kt, std::true_type{}, std::true_type{});
+    if (kt + 1 < nk) {
+        tile(kt, std::true_type{}, std::false_type{});
+        ++kt;
     }
+    tile(kt, std::false_type{}, std::false_type{});
 
     // 32x32 result layout: lane (lr, lh), register 4g+q holds row 8g + 4lh + q (weight row
     // n) and column lr (token m).
@@ -194,14 +235,14 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
         }
 }
 
-template <int BN, int BM, int BK, int STAGES, int WN, int WM, bool DUAL, typename Epi>
+template <int BN, int BM, int BK, int WN, int WM, bool DUAL, typename Epi>
 hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s, int n_begin = 0) {
     const WeightRows<bf16> W{(const bf16*)g.W.p0, (const bf16*)g.W.p1, (const bf16*)g.W.p2, g.W.end0, g.W.end1, g.W.ld};
     const WeightRows<bf16> W3{(const bf16*)g.W3.p0, (const bf16*)g.W3.p1, (const bf16*)g.W3.p2, g.W3.end0, g.W3.end1, g.W3.ld};
     constexpr int ROWS = (DUAL ? 2 : 1) * BN + BM;
-    constexpr size_t lds_bytes = (size_t)STAGES * ROWS * BK * 2;
+    constexpr size_t lds_bytes = (size_t)2 * ROWS * BK * 2;
     static_assert(lds_bytes <= 160 * 1024, "LDS");
-    auto kern = gemm_mfma_kernel<BN, BM, BK, STAGES, WN, WM, DUAL, Epi>;
+    auto kern = gemm_mfma_kernel<BN, BM, BK, WN, WM, DUAL, Epi>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
@@ -216,22 +257,23 @@ hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s, int 
 
 // Tile shapes per GEMM shape, measured on MI355X (8B-shaped layer at 2048 tokens):
 //  - wide weight matrices (Q/K/V, the vocabulary) and every GEMM with many token tiles:
-//    256 tokens x 256 or 192 weight rows, 8 waves, two 64-deep LDS stages.  192 rows is
-//    taken when it covers the 256 CUs in fewer rounds of tiles for the same work (Q/K/V at
-//    2048 tokens: 256 tiles instead of 192, 117 us instead of 150);
-//  - the SwiGLU gate/up pair: 128 rows of W1 + 128 of W3 against 256 tokens, 8 waves.  When
+//    256 tokens x 256 or 192 weight rows, 8 waves.  192 rows is taken when it covers the
+//    256 CUs in fewer rounds of tiles for the same work (Q/K/V at 2048 tokens: 256 tiles
+//    instead of 192, 117 us instead of 150);
+//  - the SwiGLU gate/up pair: 128 rows of W1 + 128 of W3 against 256 tokens, 4 waves of
+//    64 + 64 rows x 128 tokens (a third fewer LDS fragment reads than 8 waves).  When
 //    the tiles fill the CUs a few times over plus a final round less than half full (2048
 //    tokens: 896 tiles = 3.5 rounds), the weight rows of that last round go to a second
 //    launch of half-height tiles (128 tokens) that fills one round: the last round then
 //    takes about half a tile's time instead of a whole one;
 //  - N = dim outputs (WO, W2) at a few thousand tokens: 256 weight rows x 128 tokens, 4 waves
-//    of 128 x 64, three LDS stages (256 tiles at 2048 tokens; the per-tile operand traffic
-//    of 128 x 128 tiles left those GEMMs bound by the global-to-LDS copies).
+//    of 128 x 64 (256 tiles at 2048 tokens; the per-tile operand traffic of 128 x 128 tiles
+//    left those GEMMs bound by the operand copies).
 template <bool DUAL, typename Epi>
 hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
     if (g.a_pack > 0) return skinny_launch<DUAL>(g, e, s);
-    if (g.M <= 32) return launch_cfg<128, 32, 64, 3, 4, 1, DUAL>(g, e, s);
+    if (g.M <= 32) return launch_cfg<128, 32, 64, 4, 1, DUAL>(g, e, s);
     if constexpr (DUAL) {
         const int strips = (g.N + 127) / 128, mt = (g.M + 255) / 256;
         const long long tiles = (long long)strips * mt, rest = tiles % 256;
@@ -239,11 +281,11 @@ hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
             const int n_tail = (int)(strips - rest / mt) * 128;  // rows of the last round
             GemmArgs<void> head = g;
             head.N = n_tail;
-            hipError_t err = launch_cfg<128, 256, 64, 2, 2, 4, DUAL>(head, e, s);
+            hipError_t err = launch_cfg<128, 256, 64, 2, 2, DUAL>(head, e, s);
             if (err != hipSuccess) return err;
-            return launch_cfg<128, 128, 64, 3, 2, 2, DUAL>(g, e, s, n_tail);
+            return launch_cfg<128, 128, 64, 2, 2, DUAL>(g, e, s, n_tail);
         }
-        return launch_cfg<128, 256, 64, 2, 2, 4, DUAL>(g, e, s);
+        return launch_cfg<128, 256, 64, 2, 2, DUAL>(g, e, s);
     } else {
         const long long mt = (g.M + 255) / 256;
         const long long t256 = (long long)((g.N + 255) / 256) * mt;
@@ -251,10 +293,10 @@ hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
             // rounds of 256 tiles x rows per tile: the smaller wins, ties go to 256 rows
             const long long t192 = (long long)((g.N + 191) / 192) * mt;
             if (((t192 + 255) / 256) * 192 < ((t256 + 255) / 256) * 256)
-                return launch_cfg<192, 256, 64, 2, 2, 4, DUAL>(g, e, s);
-            return launch_cfg<256, 256, 64, 2, 2, 4, DUAL>(g, e, s);
+                return launch_cfg<192, 256, 64, 2, 4, DUAL>(g, e, s);
+            return launch_cfg<256, 256, 64, 2, 4, DUAL>(g, e, s);
         }
-        return launch_cfg<256, 128, 64, 3, 2, 2, DUAL>(g, e, s);
+        return launch_cfg<256, 128, 64, 2, 2, DUAL>(g, e, s);
     }
 }
 
