@@ -67,9 +67,15 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
     const int tiles = nt_m * nt_n;
     int bid = blockIdx.x;
     // workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous run of
-    // tiles (token tiles fastest) so that tiles sharing weight rows share that XCD's L2
+    // tiles, ordered in groups of up to GROUP_M token tiles x all weight strips (token
+    // tiles fastest), so that the ~32 tiles an XCD runs at once cover about 8 token tiles
+    // x 4 weight strips and share their panels in that XCD's L2
     if (tiles % 8 == 0) bid = (bid & 7) * (tiles >> 3) + (bid >> 3);
-    const int tile_m = bid % nt_m, tile_n = bid / nt_m;
+    constexpr int GROUP_M = 8;
+    const int per_group = GROUP_M * nt_n;
+    const int first_m = (bid / per_group) * GROUP_M;
+    const int gsize = min(nt_m - first_m, GROUP_M);
+    const int tile_m = first_m + (bid % per_group) % gsize, tile_n = (bid % per_group) / gsize;
     const int n0 = n_begin + tile_n * BN, m0 = tile_m * BM;
 
     // this lane's source address for each of its wave's copies of a stage
