@@ -249,7 +249,9 @@ hipError_t gemm_residual_split(Dt dt, const GemmArgs<void>& g, float* part, int 
 //   - vocabulary projection: 1 row 197 -> 176 us with RT 4; batch 32 209 -> 197 us with RT 8
 //     (against RT 4);
 //   - gate/up pair: batch 4 50 -> 45 us with RT 2; batch 32 RT 2 (RT 4 no faster);
-//   - Q/K/V with RT 2 at batch 4: 17 -> 21 us, so RT 1.
+//   - Q/K/V: at batch 4 RT 2 is slower (17 -> 21 us), so RT 1; from 17 rows on (two or
+//     more 16-row blocks) two activation bytes per weight byte make RT 2 pay (batch 32:
+//     24.6 -> 21.7 us).
 template <bool DUAL, typename Epi>
 hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     if (g.a_pack != act_pack(Dt::BF16, g.M, g.N, g.K)) return hipErrorInvalidValue;
@@ -268,8 +270,9 @@ hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
         if (mb == 1) return launch_mb<1, 1, DUAL>(g, e, s);
         if (mb == 2 && wide && g.N % (SK_ROWS * 8) == 0) return launch_mb<8, 2, DUAL>(g, e, s);
         if (mb == 2 && wide && g.N % (SK_ROWS * 4) == 0) return launch_mb<4, 2, DUAL>(g, e, s);
+        if (mb == 2 && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 2, DUAL>(g, e, s);
         if (mb == 2) return launch_mb<1, 2, DUAL>(g, e, s);
-        if (wide && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 4, DUAL>(g, e, s);
+        if (g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 4, DUAL>(g, e, s);
         return launch_mb<1, 4, DUAL>(g, e, s);
     }
 }

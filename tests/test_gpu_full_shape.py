@@ -59,7 +59,8 @@ def test_prefill_8b_widths_2048_tokens():
     assert_rows_close(vc.reshape(8, -1), caches[0].v[1].reshape(8, -1), BF16_TOL, "V cache, layer 2")
 
 
-@pytest.mark.parametrize("B,ctx,rows,steps", [(32, 4096, (0, 31), 3), (4, 8192, (0,), 2)])
+@pytest.mark.parametrize("B,ctx,rows,steps", [(32, 4096, (0, 31), 3), (4, 8192, (0,), 2),
+                                               (48, 512, (0, 47), 2)])
 def test_decode_8b_widths(B, ctx, rows, steps):
     say(f"8B widths, 1 layer, prefill {B} x {ctx}, then {steps} teacher-forced decode steps")
     spec = _spec(1)
