@@ -37,14 +37,18 @@ def _oracle_weights(synth, layers):
     return {n: synth.as_float(n, np.float32) for n in names}
 
 
-def test_prefill_8b_widths_2048_tokens():
-    say("8B widths, 2 layers, prefill 1 x 2048 (benchmark launch shapes), full vocabulary")
+@pytest.mark.parametrize("S", [2048, 2600])
+def test_prefill_8b_widths(S):
+    """S = 2048: the benchmark's launch shapes.  S = 2600: 11 token tiles of 256 and 21 of
+    128, so the GEMMs' grouped tile order ends in a partial group of 3 (resp. 5) token
+    tiles, and every M tail is ragged."""
+    say(f"8B widths, 2 layers, prefill 1 x {S}, full vocabulary")
     spec = _spec(2)
-    m, synth = build_model(spec, 3, max_batch=1, max_seq=2048, max_tokens=2048, cache=False)
-    toks = syn.tokens(3, 1, 2048, spec.vocab_size)
+    m, synth = build_model(spec, 3, max_batch=1, max_seq=S, max_tokens=S, cache=False)
+    toks = syn.tokens(3, 1, S, spec.vocab_size)
     got = m.prefill(torch.from_numpy(toks).cuda()).cpu().numpy()
-    kc = m.cache_k(1)[0, :, :2048].float().cpu().numpy()
-    vc = m.cache_v(1)[0, :, :2048].float().cpu().numpy()
+    kc = m.cache_k(1)[0, :, :S].float().cpu().numpy()
+    vc = m.cache_v(1)[0, :, :S].float().cpu().numpy()
     m.sync_status()
     del m
     W = _oracle_weights(synth, 2)
@@ -52,7 +56,7 @@ def test_prefill_8b_widths_2048_tokens():
     ref, caches = O.prefill(toks, W, spec, dtype=np.float32)
     assert_rows_close(got, ref, BF16_TOL, "last-token logits")
     check_argmax(np.argmax(got, -1), got, ref, "last token")
-    # layer-2 cache at every position, normwise per KV head ([2048, 128] blocks: a single
+    # layer-2 cache at every position, normwise per KV head ([S, 128] blocks: a single
     # 128-wide row is too short for a normwise maximum to measure the same thing as a
     # 128256-wide logit row; after one layer of bf16 noise its tail reaches ~2.4%)
     assert_rows_close(kc.reshape(8, -1), caches[0].k[1].reshape(8, -1), BF16_TOL, "K cache, layer 2")
