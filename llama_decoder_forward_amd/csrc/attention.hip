@@ -514,6 +514,9 @@ __global__ __launch_bounds__(NWV * 64) void attn_decode_mfma_kernel(
 }
 
 // Merge the splits of one (sequence, head): o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// Thread t owns split t for the weights and dimension t for the sum; the splits are summed
+// in order, 16 loads in flight at a time (the partials were just written and sit in L2).
+constexpr int MERGE_BATCH = 16;
 template <typename T>
 __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const float* __restrict__ part,
                                                                 T* __restrict__ out, int start_pos,
@@ -521,33 +524,36 @@ __global__ __launch_bounds__(128) void attn_decode_merge_kernel(const float* __r
                                                                 int pos_stride, int max_pos, int H,
                                                                 int d, int max_splits, int chunk,
                                                                 int out_pack) {
-    __shared__ float wts[128];
-    __shared__ float red[2];
+    __shared__ float wts[128 + MERGE_BATCH];
+    __shared__ float red_m[2], red_l[2];
     const int h = blockIdx.x, b = blockIdx.y;
     const int pos = max(seq_pos(pos_dev, pos_stride, b, start_pos, max_pos), 0);
-    const int nsplit = (pos + 1 + chunk - 1) / chunk;  // <= 128
+    const int nsplit = (pos + 1 + chunk - 1) / chunk;  // 1 .. 128
     const float* pp = part + (size_t)(b * H + h) * max_splits * (d + 2);
     const int t = threadIdx.x;
     const float mt = t < nsplit ? pp[(size_t)t * (d + 2)] : -INFINITY;
-    wts[t] = mt;
+    const float wmax = wave_max(mt);
+    if ((t & 63) == 0) red_m[t >> 6] = wmax;
     __syncthreads();
-    if (t == 0) {
-        float M = -INFINITY;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, wts[s]);
-        red[0] = M;
-    }
-    __syncthreads();
-    const float w = t < nsplit ? exp2f(mt - red[0]) : 0.0f;
+    const float M = fmaxf(red_m[0], red_m[1]);
+    const float w = t < nsplit ? exp2f(mt - M) : 0.0f;
     const float lw = t < nsplit ? w * pp[(size_t)t * (d + 2) + 1] : 0.0f;
-    __syncthreads();
     wts[t] = w;
+    if (t < MERGE_BATCH) wts[128 + t] = 0.0f;
     const float lsum = wave_sum(lw);
-    if ((t & 63) == 0) red[t >> 6] = lsum;  // red[0] (the max) is no longer needed
+    if ((t & 63) == 0) red_l[t >> 6] = lsum;
     __syncthreads();
-    const float den = red[0] + red[1];
+    const float den = red_l[0] + red_l[1];
     for (int i = t; i < d; i += blockDim.x) {
         float num = 0.0f;
-        for (int s = 0; s < nsplit; ++s) num += wts[s] * pp[(size_t)s * (d + 2) + 2 + i];
+        for (int s0 = 0; s0 < nsplit; s0 += MERGE_BATCH) {
+            float v[MERGE_BATCH];
+#pragma unroll
+            for (int j = 0; j < MERGE_BATCH; ++j)  // past the last split: reread it, weight 0
+                v[j] = pp[(size_t)min(s0 + j, nsplit - 1) * (d + 2) + 2 + i];
+#pragma unroll
+            for (int j = 0; j < MERGE_BATCH; ++j) num += wts[s0 + j] * v[j];
+        }
         out[act_offset(b, h * d + i, H * d, out_pack)] = from_f32<T>(num / den);
     }
 }
