@@ -6,7 +6,6 @@
 #include <cstdarg>
 #include <cstdio>
 #include <new>
-#include <string>
 #include <vector>
 
 #include "llama_mi355x.h"
@@ -14,15 +13,15 @@
 
 namespace {
 
-thread_local std::string g_last_error;
+// Nothing here may throw across the C ABI: the message buffer is a fixed array, and the
+// two containers that grow (the layer table, the profiling events) catch allocation failure.
+thread_local char g_last_error[512];
 
 llama_status fail(llama_status st, const char* fmt, ...) {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
     va_end(ap);
-    g_last_error = buf;
     return st;
 }
 
@@ -170,7 +169,12 @@ struct ProfScope {
             for (int i = 0; i < 2; ++i) {
                 hipEvent_t e;
                 if (hipEventCreate(&e) != hipSuccess) return;
-                m->prof_events.push_back(e);
+                try {
+                    m->prof_events.push_back(e);
+                } catch (...) {  // no profiling for this launch
+                    (void)hipEventDestroy(e);
+                    return;
+                }
             }
         }
         hipEvent_t start = m->prof_events[m->prof_used];
@@ -359,7 +363,12 @@ llama_status llama_init_weights(const llama_config* cfg, const llama_weights* w,
     llama_model* m = new (std::nothrow) llama_model();
     if (!m) return fail(LLAMA_ERR_ALLOC, "handle allocation failed");
     m->cfg = *cfg;
-    m->layers.assign(w->layers, w->layers + cfg->n_layers);
+    try {
+        m->layers.assign(w->layers, w->layers + cfg->n_layers);
+    } catch (...) {
+        delete m;
+        return fail(LLAMA_ERR_ALLOC, "layer table allocation failed");
+    }
     m->tok_embeddings = w->tok_embeddings;
     m->norm = w->norm;
     m->output = w->output;
@@ -523,6 +532,6 @@ void llama_free(llama_model* m) {
     delete m;
 }
 
-const char* llama_last_error(void) { return g_last_error.c_str(); }
+const char* llama_last_error(void) { return g_last_error; }
 
 }  // extern "C"
