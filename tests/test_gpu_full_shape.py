@@ -18,7 +18,8 @@ from oracle import llama_oracle as O
 
 from gpu_util import BF16_TOL, assert_rows_close, build_model, check_argmax, require_gpu, say
 
-pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+# a hung GPU call ends the run (thread method) instead of stalling it
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900, method="thread")]
 
 
 @pytest.fixture(scope="module", autouse=True)
