@@ -153,6 +153,56 @@ def cpu_baseline(spec, seed: int, S: int, n_layers_sample: int):
             "seconds_measured": t3 - t0}
 
 
+def long_context(spec, weights, prefill_runs: int, decode_steps: int) -> dict:
+    """4 sequences of 8192 tokens prefilled in one call (timed over prefill_runs calls after
+    one warmup), then decode_steps greedy steps of the batch against those caches
+    (llama_generate, timed after one warmup); a model of its own, with the cache sized for
+    8192 + decode_steps positions."""
+    import torch
+    from llama_decoder_forward_amd import binding as bd
+    from llama_decoder_forward_amd import synthetic as syn
+
+    L_B, L_S = 4, 8192
+    stream = torch.cuda.current_stream()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ml = bd.Model(spec, weights, max_batch=L_B, max_seq=L_S + decode_steps, max_tokens=L_B * L_S)
+    ltoks = torch.from_numpy(syn.tokens(5, L_B, L_S, spec.vocab_size)).cuda()
+    lg = ml.prefill(ltoks)                            # warmup
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(prefill_runs):
+        lg = ml.prefill(ltoks)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    lp_ms = start.elapsed_time(stop) / prefill_runs
+    first = lg.argmax(-1).to(torch.int32).contiguous()
+    ml.generate(first, L_S, decode_steps)             # warmup (same positions)
+    torch.cuda.synchronize()
+    start.record(stream)
+    ml.generate(first, L_S, decode_steps)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ld_ms = start.elapsed_time(stop)
+    ml.sync_status()
+    ml.free()
+    lfl = prefill_flops(spec, L_B, L_S)
+    lbytes = decode_bytes(spec, L_B, L_S + 1, decode_steps)
+    log(f"long context: prefill {lp_ms:.1f} ms, decode {ld_ms / decode_steps:.3f} ms/step")
+    return {
+        "workload": f"llama3-8b-shaped prefill of {L_B} x {L_S} tokens in one call, then "
+                    f"{decode_steps} greedy decode steps of the batch (llama_generate)",
+        "prefill": {"value": L_B * L_S / (lp_ms * 1e-3), "unit": "tokens/s",
+                    "ms_per_step": lp_ms, "steps": prefill_runs,
+                    "mfma_frac": lfl / (lp_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                    "tflops": lfl / (lp_ms * 1e-3) / 1e12},
+        "decode": {"value": L_B * decode_steps / (ld_ms * 1e-3), "unit": "tokens/s",
+                   "ms_per_step": ld_ms / decode_steps, "steps": decode_steps, "batch": L_B,
+                   "context": [L_S + 1, L_S + decode_steps],
+                   "hbm_gbs": lbytes / (ld_ms * 1e-3) / 1e9,
+                   "hbm_frac": lbytes / (ld_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +215,9 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-long", action="store_true",
                     help="skip the long-context leg (4 x 8192 prefill, then batch-4 decode)")
+    ap.add_argument("--long-only", action="store_true",
+                    help="run only the long-context leg, short (1 timed prefill, 8 decode steps), "
+                         "and print its object; for rocprofv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -200,6 +253,11 @@ def main() -> int:
         del src, dst
     spec = syn.LLAMA3_8B
     seed = 3
+    if args.long_only:
+        weights = bd.upload_weights(syn.SyntheticWeights(spec, seed, cache=False))
+        print(json.dumps({"long_context": long_context(spec, weights, prefill_runs=1,
+                                                       decode_steps=8)}), flush=True)
+        return 0
     dec_B, dec_ctx, dec_steps = args.decode_batch, args.decode_ctx, args.decode_steps
     if args.profile_only:
         dec_steps = min(dec_steps, 8)
@@ -374,50 +432,10 @@ def main() -> int:
             }
 
     # ---------------------------------------------------------------- long context
-    # 4 sequences of 8192 tokens prefilled in one call (timed), then 64 greedy decode steps
-    # of the batch against those caches (llama_generate, timed); a model of its own, with
-    # the cache sized for 8192 + 64 positions
     if not args.no_long and not args.profile_only:
-        L_B, L_S, L_steps = 4, 8192, 64
         del m
         torch.cuda.empty_cache()
-        ml = bd.Model(spec, weights, max_batch=L_B, max_seq=L_S + L_steps, max_tokens=L_B * L_S)
-        ltoks = torch.from_numpy(syn.tokens(5, L_B, L_S, spec.vocab_size)).cuda()
-        lg = ml.prefill(ltoks)                            # warmup
-        torch.cuda.synchronize()
-        l_runs = 2
-        start.record(stream)
-        for _ in range(l_runs):
-            lg = ml.prefill(ltoks)
-        stop.record(stream)
-        torch.cuda.synchronize()
-        lp_ms = start.elapsed_time(stop) / l_runs
-        first = lg.argmax(-1).to(torch.int32).contiguous()
-        ml.generate(first, L_S, L_steps)                  # warmup (same positions)
-        torch.cuda.synchronize()
-        start.record(stream)
-        ml.generate(first, L_S, L_steps)
-        stop.record(stream)
-        torch.cuda.synchronize()
-        ld_ms = start.elapsed_time(stop)
-        ml.sync_status()
-        lfl = prefill_flops(spec, L_B, L_S)
-        lbytes = decode_bytes(spec, L_B, L_S + 1, L_steps)
-        log(f"long context: prefill {lp_ms:.1f} ms, decode {ld_ms / L_steps:.3f} ms/step")
-        result["long_context"] = {
-            "workload": f"llama3-8b-shaped prefill of {L_B} x {L_S} tokens in one call, then "
-                        f"{L_steps} greedy decode steps of the batch (llama_generate)",
-            "prefill": {"value": L_B * L_S / (lp_ms * 1e-3), "unit": "tokens/s",
-                        "ms_per_step": lp_ms, "steps": l_runs,
-                        "mfma_frac": lfl / (lp_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                        "tflops": lfl / (lp_ms * 1e-3) / 1e12},
-            "decode": {"value": L_B * L_steps / (ld_ms * 1e-3), "unit": "tokens/s",
-                       "ms_per_step": ld_ms / L_steps, "steps": L_steps, "batch": L_B,
-                       "context": [L_S + 1, L_S + L_steps],
-                       "hbm_gbs": lbytes / (ld_ms * 1e-3) / 1e9,
-                       "hbm_frac": lbytes / (ld_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
-        }
-        del ml
+        result["long_context"] = long_context(spec, weights, prefill_runs=2, decode_steps=64)
         m = None
 
     # ---------------------------------------------------------------- CPU oracle baseline
