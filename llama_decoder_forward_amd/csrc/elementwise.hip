@@ -52,71 +52,118 @@ hipError_t embed(Dt dt, const int* tokens, const void* E, float* x, int rows, in
 }
 
 // y = x * 1/sqrt(mean(x^2) + eps) * w per row (article, section 分词器与编码; also the
-// pitchhut deep-dive's layer-normalisation example).  One 256-thread block per row; the
-// row lives in registers between the two passes.  D % 8 == 0, D <= 256*8*MAXV.
+// pitchhut deep-dive's layer-normalisation example).  One block of NT threads per row, each
+// thread holding MAXV chunks of 8 values in registers between the two passes (NT * 8 * MAXV
+// >= D, D % 8 == 0).
 //
 // With nsplit > 0 the row first takes the pending split-K sums of the residual GEMM that
-// wrote it: x' = x + parts[0] + parts[1] + ... (in that order), stored to x_out.
-template <typename T, int MAXV>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int in_step, int in_off,
-                                                      const T* w, T* y, int y_pack, int D,
-                                                      float eps, const float* parts, int nsplit,
-                                                      size_t split_stride, float* x_out) {
+// wrote it: x' = x + parts[0] + parts[1] + ... (in that order), stored to x_out.  NSMAX > 0
+// handles nsplit <= NSMAX with every load of the row (x and all splits) issued before the
+// first add, so a decode-sized launch (few rows) waits for one round trip to memory instead
+// of one per chunk; NSMAX < 0 takes any nsplit in groups of four.
+template <typename T, int NT, int MAXV, int NSMAX>
+__global__ __launch_bounds__(NT) void rmsnorm_kernel(const float* x, int in_step, int in_off,
+                                                     const T* w, T* y, int y_pack, int D,
+                                                     float eps, const float* parts, int nsplit,
+                                                     size_t split_stride, float* x_out) {
     const int r = blockIdx.x;
     const size_t row = ((size_t)r * in_step + in_off) * D;
     const float* xr = x + row;
     float v[MAXV][8];
     float ss = 0.0f;
-#pragma unroll
-    for (int c = 0; c < MAXV; ++c) {
-        const int i = (threadIdx.x + c * 256) * 8;
-        if (i < D) {
-            const f32x4 a = *reinterpret_cast<const f32x4*>(xr + i);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(xr + i + 4);
-            v[c][0] = a[0]; v[c][1] = a[1]; v[c][2] = a[2]; v[c][3] = a[3];
-            v[c][4] = b[0]; v[c][5] = b[1]; v[c][6] = b[2]; v[c][7] = b[3];
-            // splits in groups of four, each group's loads issued together (indices past
-            // the last split re-read it and are not added)
-            for (int z0 = 0; z0 < nsplit; z0 += 4) {
-                f32x4 pa[4], pb[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int z = z0 + u < nsplit ? z0 + u : nsplit - 1;
-                    const float* pr = parts + z * split_stride + row + i;
-                    pa[u] = *reinterpret_cast<const f32x4*>(pr);
-                    pb[u] = *reinterpret_cast<const f32x4*>(pr + 4);
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    if (z0 + u < nsplit) {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) { v[c][j] += pa[u][j]; v[c][4 + j] += pb[u][j]; }
-                    }
-            }
-            if (nsplit > 0) {
-                store4(x_out + row + i, v[c]);
-                store4(x_out + row + i + 4, v[c] + 4);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) ss += v[c][j] * v[c][j];
-        }
-    }
-    // the weights do not depend on the sum: load them before the block-wide reduction
+    // The loads are unconditional (chunks past D re-read the last one and are not used): a
+    // branch around a load makes the compiler wait for every load in flight at the join.
+    // The weights do not depend on the row: their loads go out first.
     float wv[MAXV][8];
 #pragma unroll
     for (int c = 0; c < MAXV; ++c) {
-        const int i = (threadIdx.x + c * 256) * 8;
-        if (i < D) load8(w + i, wv[c]);
+        const int i = (threadIdx.x + c * NT) * 8;
+        load8(w + (i < D ? i : D - 8), wv[c]);
     }
-    __shared__ float red[4];
+    if constexpr (NSMAX >= 0) {
+        // indices past the last split re-read it and are not added
+        constexpr int NP = NSMAX > 0 ? NSMAX : 1;
+        f32x4 xa[MAXV][2], pa[MAXV][NP][2];
+#pragma unroll
+        for (int c = 0; c < MAXV; ++c) {
+            const int i0 = (threadIdx.x + c * NT) * 8, i = i0 < D ? i0 : D - 8;
+            xa[c][0] = *reinterpret_cast<const f32x4*>(xr + i);
+            xa[c][1] = *reinterpret_cast<const f32x4*>(xr + i + 4);
+#pragma unroll
+            for (int u = 0; u < NSMAX; ++u) {
+                const int z = u < nsplit ? u : nsplit - 1;
+                const float* pr = parts + z * split_stride + row + i;
+                pa[c][u][0] = *reinterpret_cast<const f32x4*>(pr);
+                pa[c][u][1] = *reinterpret_cast<const f32x4*>(pr + 4);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < MAXV; ++c) {
+            const int i = (threadIdx.x + c * NT) * 8;
+            if (i < D) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) { v[c][j] = xa[c][0][j]; v[c][4 + j] = xa[c][1][j]; }
+#pragma unroll
+                for (int u = 0; u < NSMAX; ++u)
+                    if (u < nsplit) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) { v[c][j] += pa[c][u][0][j]; v[c][4 + j] += pa[c][u][1][j]; }
+                    }
+                if (nsplit > 0) {
+                    store4(x_out + row + i, v[c]);
+                    store4(x_out + row + i + 4, v[c] + 4);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) ss += v[c][j] * v[c][j];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < MAXV; ++c) {
+            const int i = (threadIdx.x + c * NT) * 8;
+            if (i < D) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(xr + i);
+                const f32x4 b = *reinterpret_cast<const f32x4*>(xr + i + 4);
+                v[c][0] = a[0]; v[c][1] = a[1]; v[c][2] = a[2]; v[c][3] = a[3];
+                v[c][4] = b[0]; v[c][5] = b[1]; v[c][6] = b[2]; v[c][7] = b[3];
+                // splits in groups of four, each group's loads issued together
+                for (int z0 = 0; z0 < nsplit; z0 += 4) {
+                    f32x4 pa[4], pb[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int z = z0 + u < nsplit ? z0 + u : nsplit - 1;
+                        const float* pr = parts + z * split_stride + row + i;
+                        pa[u] = *reinterpret_cast<const f32x4*>(pr);
+                        pb[u] = *reinterpret_cast<const f32x4*>(pr + 4);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (z0 + u < nsplit) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) { v[c][j] += pa[u][j]; v[c][4 + j] += pb[u][j]; }
+                        }
+                }
+                if (nsplit > 0) {
+                    store4(x_out + row + i, v[c]);
+                    store4(x_out + row + i + 4, v[c] + 4);
+                }
+#pragma unroll
+                for (int j = 0; j < 8; ++j) ss += v[c][j] * v[c][j];
+            }
+        }
+    }
+    constexpr int NWAVE = NT / 64;
+    __shared__ float red[NWAVE];
     ss = wave_sum(ss);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
     __syncthreads();
-    const float total = red[0] + red[1] + red[2] + red[3];
+    float total = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NWAVE; ++k) total += red[k];
     const float inv = 1.0f / sqrtf(total / (float)D + eps);
 #pragma unroll
     for (int c = 0; c < MAXV; ++c) {
-        const int i = (threadIdx.x + c * 256) * 8;
+        const int i = (threadIdx.x + c * NT) * 8;
         if (i < D) {
             float o[8];
 #pragma unroll
@@ -128,18 +175,34 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int in_ste
     }
 }
 
+template <typename T, int NT, int MAXV>
+static void rmsnorm_launch(const float* x, int step, int off, const T* w, T* y, int y_pack,
+                           int rows, int D, float eps, const float* parts, int nsplit,
+                           size_t split_stride, float* x_out, hipStream_t s) {
+    if (nsplit == 0)
+        rmsnorm_kernel<T, NT, MAXV, 0><<<rows, NT, 0, s>>>(x, step, off, w, y, y_pack, D, eps,
+                                                          parts, nsplit, split_stride, x_out);
+    else if (nsplit <= 4)
+        rmsnorm_kernel<T, NT, MAXV, 4><<<rows, NT, 0, s>>>(x, step, off, w, y, y_pack, D, eps,
+                                                          parts, nsplit, split_stride, x_out);
+    else
+        rmsnorm_kernel<T, NT, MAXV, -1><<<rows, NT, 0, s>>>(x, step, off, w, y, y_pack, D, eps,
+                                                           parts, nsplit, split_stride, x_out);
+}
+
+// one 8-value chunk per thread up to D = 8192, then two (D <= 16384, the largest dim taken)
 template <typename T>
 static hipError_t rmsnorm_t(const float* x, int step, int off, const T* w, T* y, int y_pack,
                             int rows, int D, float eps, const float* parts, int nsplit,
                             size_t split_stride, float* x_out, hipStream_t s) {
-#define LK_RMSNORM(V)                                                                         \
-    rmsnorm_kernel<T, V><<<rows, 256, 0, s>>>(x, step, off, w, y, y_pack, D, eps, parts, nsplit, \
-                                              split_stride, x_out)
-    if (D <= 2048) LK_RMSNORM(1);
-    else if (D <= 4096) LK_RMSNORM(2);
-    else if (D <= 8192) LK_RMSNORM(4);
-    else LK_RMSNORM(8);
-#undef LK_RMSNORM
+    if (D <= 2048)
+        rmsnorm_launch<T, 256, 1>(x, step, off, w, y, y_pack, rows, D, eps, parts, nsplit, split_stride, x_out, s);
+    else if (D <= 4096)
+        rmsnorm_launch<T, 512, 1>(x, step, off, w, y, y_pack, rows, D, eps, parts, nsplit, split_stride, x_out, s);
+    else if (D <= 8192)
+        rmsnorm_launch<T, 1024, 1>(x, step, off, w, y, y_pack, rows, D, eps, parts, nsplit, split_stride, x_out, s);
+    else
+        rmsnorm_launch<T, 1024, 2>(x, step, off, w, y, y_pack, rows, D, eps, parts, nsplit, split_stride, x_out, s);
     return hipGetLastError();
 }
 
