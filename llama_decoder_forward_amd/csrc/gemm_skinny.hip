@@ -248,7 +248,8 @@ hipError_t gemm_residual_split(Dt dt, const GemmArgs<void>& g, float* part, int 
 // gate/up pair).  Measured on MI355X, 8B shape:
 //   - vocabulary projection: 1 row 197 -> 176 us with RT 4; batch 32 209 -> 197 us with RT 8
 //     (against RT 4);
-//   - gate/up pair: batch 4 50 -> 45 us with RT 2; batch 32 RT 2 (RT 4 no faster);
+//   - gate/up pair: batch 4 50 -> 45 us with RT 2; batch 32 52.9 -> 51.0 us with RT 4 and
+//     4 waves per strip (RT 4 with the 8 waves its strip count would get: no faster);
 //   - Q/K/V: at batch 4 RT 2 is slower (17 -> 21 us), so RT 1; from 17 rows on (two or
 //     more 16-row blocks) two activation bytes per weight byte make RT 2 pay (batch 32:
 //     24.6 -> 21.7 us).
@@ -258,6 +259,12 @@ hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     const int mb = g.a_pack < 16 ? 1 : g.a_pack / 16;  // 16-row MFMA column blocks
     const bool wide = g.N >= 16384;
     if constexpr (DUAL) {
+        if (mb == 2 && g.N % (SK_ROWS * 4) == 0) {
+            const int strips = g.N / (SK_ROWS * 4);
+            gemm_skinny_kernel<4, 4, 2, DUAL, 96, Epi><<<strips, 256, 0, s>>>(
+                (const bf16*)g.A, g.a_pack, bf16_rows(g.W), bf16_rows(g.W3), g.M, g.N, g.K, e);
+            return hipGetLastError();
+        }
         if (mb <= 2 && g.N % (SK_ROWS * 2) == 0) {
             if (mb == 1) return launch_mb<2, 1, DUAL>(g, e, s);
             return launch_mb<2, 2, DUAL>(g, e, s);
