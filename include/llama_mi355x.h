@@ -162,7 +162,14 @@ llama_status llama_decode_step_ragged(llama_model *m, const int32_t *tokens, int
  * position pos+k on the previous step's argmax.  The position and step index live in
  * device memory, so the whole loop is enqueued at once with no host synchronisation.
  * Writes out_tokens[k*B + b], the argmax of step k; if logits is not NULL also the logits
- * [n_steps,B,V].  Needs pos + n_steps <= max_seq. */
+ * [n_steps,B,V].  Needs pos + n_steps <= max_seq.
+ *
+ * Stream capture: after the model's first call (its one-time set-up: flags, rotary table,
+ * cache zero fill), llama_generate, llama_decode_step and llama_decode_step_ragged enqueue
+ * kernel launches only (no memset, allocation or host synchronisation), so they may be
+ * recorded into a stream capture and the graph replayed.  A replay repeats the recorded
+ * arguments: the same start position for llama_generate and llama_decode_step, the
+ * positions then in device memory for llama_decode_step_ragged. */
 llama_status llama_generate(llama_model *m, const int32_t *tokens, int32_t B, int32_t pos,
                             int32_t n_steps, int32_t *out_tokens, float *logits,
                             hipStream_t stream);
