@@ -143,6 +143,31 @@ def test_bf16_teacher_forced_decode():
     m.sync_status()
 
 
+@pytest.mark.parametrize("B", [20, 32])
+def test_bf16_teacher_forced_decode_two_row_blocks(B):
+    # 17..32 rows: two 16-row activation blocks (the second partly padding at B = 20), which
+    # the weight-streaming GEMMs serve with more row tiles per wave (RT 2 for Q/K/V, RT 4
+    # for the gate/up pair), and a split decode attention grid
+    S, steps = 24, 3
+    say(f"small bf16 stack: prefill S={S} then {steps} teacher-forced decode steps, B={B}")
+    spec = small_bf16_spec()
+    m, synth = build_model(spec, 40 + B, max_batch=B, max_seq=32, max_tokens=B * S)
+    toks = syn.tokens(40 + B, B, S, spec.vocab_size)
+    W = syn.FloatView(synth)
+    ref0, caches = O.prefill(toks, W, spec, capacity=S + steps)
+    got0 = m.prefill(torch.from_numpy(toks).cuda()).cpu().numpy()
+    assert_rows_close(got0, ref0, BF16_TOL, "prefill last logits")
+    cur = O.argmax(ref0).astype(np.int32)
+    for k in range(steps):
+        ref = O.decode_step(cur, S + k, W, spec, caches)
+        nxt, lg = m.decode_step(torch.from_numpy(cur).cuda(), S + k)
+        lg = lg.cpu().numpy()
+        assert_rows_close(lg, ref, BF16_TOL, f"decode step {k}")
+        check_argmax(nxt.cpu().numpy(), lg, ref, f"decode step {k}")
+        cur = O.argmax(ref).astype(np.int32)
+    m.sync_status()
+
+
 def test_bf16_long_context_decode_multiple_splits():
     say("small bf16 stack: prefill S=600 (several decode splits, ragged) then 3 decode steps, B=2")
     spec = small_bf16_spec()
