@@ -272,9 +272,11 @@ hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s, int 
 //    tokens: 896 tiles = 3.5 rounds), the weight rows of that last round go to a second
 //    launch of half-height tiles (128 tokens) that fills one round: the last round then
 //    takes about half a tile's time instead of a whole one;
-//  - N = dim outputs (WO, W2) at a few thousand tokens: 256 weight rows x 128 tokens, 4 waves
-//    of 128 x 64 (256 tiles at 2048 tokens; the per-tile operand traffic of 128 x 128 tiles
-//    left those GEMMs bound by the operand copies).
+//  - N = dim outputs (WO, W2) at a few thousand tokens: 256 weight rows x 128 tokens, 8 waves
+//    (4 x 2) of 64 x 64 (256 tiles at 2048 tokens; the per-tile operand traffic of 128 x 128
+//    tiles left those GEMMs bound by the operand copies).  Two waves per SIMD against one
+//    for 4 waves of 128 x 64: WO 82 -> 78 us and W2 245 -> 237 us at 2048 tokens; 2 x 4
+//    waves gained half as much.
 template <bool DUAL, typename Epi>
 hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     if (g.M == 0) return hipSuccess;
@@ -302,7 +304,7 @@ hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
                 return launch_cfg<192, 256, 64, 2, 4, DUAL>(g, e, s);
             return launch_cfg<256, 256, 64, 2, 4, DUAL>(g, e, s);
         }
-        return launch_cfg<256, 128, 64, 2, 2, DUAL>(g, e, s);
+        return launch_cfg<256, 128, 64, 4, 2, DUAL>(g, e, s);
     }
 }
 
