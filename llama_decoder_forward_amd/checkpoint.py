@@ -35,18 +35,27 @@ class CheckpointError(ValueError):
     """A checkpoint directory that does not hold the expected tensors."""
 
 
-def ffn_hidden_from_params(dim: int, multiple_of: int, ffn_dim_multiplier=None) -> int:
-    """FFN width of the Llama-3 recipe: 2/3 of 4*dim, scaled by ffn_dim_multiplier,
-    rounded up to a multiple of multiple_of (4096, 1024, 1.3 -> 14336)."""
-    hidden = int(2 * (4 * dim) / 3)
-    if ffn_dim_multiplier is not None:
-        hidden = int(ffn_dim_multiplier * hidden)
-    return multiple_of * ((hidden + multiple_of - 1) // multiple_of)
+def params_admit_ffn_width(params: dict, width: int) -> bool:
+    """Whether a stored SwiGLU width agrees with params.json.
+
+    params.json names no width, only ``multiple_of`` and ``ffn_dim_multiplier``.  The
+    stored width must be a whole number of ``multiple_of`` blocks, and the smallest such
+    number that still covers the SwiGLU width of the recipe: two thirds of four times
+    dim, scaled by the multiplier (so that width - multiple_of falls short of it).  With no
+    ``multiple_of`` in the file nothing is checked.
+    """
+    if "multiple_of" not in params:
+        return True
+    block = int(params["multiple_of"])
+    need = (8 * int(params["dim"])) // 3
+    if params.get("ffn_dim_multiplier") is not None:
+        need = int(float(params["ffn_dim_multiplier"]) * need)
+    return block > 0 and width % block == 0 and width - block < need <= width
 
 
-def spec_from_params(params: dict, dtype: str = "bf16", ffn_hidden: int | None = None) -> ModelSpec:
-    """ModelSpec of a params.json dict. ffn_hidden, if given (the stored W1 rows), must
-    agree with the width params.json implies when it names multiple_of."""
+def spec_from_params(params: dict, ffn_hidden: int, dtype: str = "bf16") -> ModelSpec:
+    """ModelSpec of a params.json dict and the stored SwiGLU width (the rows of
+    ``layers.0.feed_forward.w1.weight``), which must agree with params.json."""
     try:
         dim, n_layers, n_heads = int(params["dim"]), int(params["n_layers"]), int(params["n_heads"])
         vocab = int(params["vocab_size"])
@@ -56,15 +65,10 @@ def spec_from_params(params: dict, dtype: str = "bf16", ffn_hidden: int | None =
     if dim <= 0 or n_heads <= 0 or dim % n_heads != 0 or n_heads % n_kv != 0 or vocab <= 0:
         raise CheckpointError(f"inconsistent params: dim {dim}, n_heads {n_heads}, "
                               f"n_kv_heads {n_kv}, vocab_size {vocab}")
-    derived = None
-    if "multiple_of" in params:
-        derived = ffn_hidden_from_params(dim, int(params["multiple_of"]), params.get("ffn_dim_multiplier"))
-    if ffn_hidden is None:
-        if derived is None:
-            raise CheckpointError("params.json names no multiple_of and no FFN width was given")
-        ffn_hidden = derived
-    elif derived is not None and derived != ffn_hidden:
-        raise CheckpointError(f"stored FFN width {ffn_hidden} != {derived} from params.json")
+    if ffn_hidden <= 0 or not params_admit_ffn_width(params, ffn_hidden):
+        raise CheckpointError(f"stored FFN width {ffn_hidden} does not follow from params.json "
+                              f"(multiple_of {params.get('multiple_of')}, ffn_dim_multiplier "
+                              f"{params.get('ffn_dim_multiplier')})")
     return ModelSpec(dim=dim, n_layers=n_layers, n_heads=n_heads, n_kv_heads=n_kv,
                      head_dim=dim // n_heads, ffn_hidden=int(ffn_hidden), vocab_size=vocab,
                      norm_eps=float(params.get("norm_eps", 1e-5)),
@@ -116,7 +120,9 @@ def load_checkpoint(directory: str, dtype: str = "bf16", device="cuda"):
         params = json.load(f)
     state, src = _open_state(directory)
     w1 = state.get("layers.0.feed_forward.w1.weight")
-    spec = spec_from_params(params, dtype, ffn_hidden=None if w1 is None else int(w1.shape[0]))
+    if w1 is None or w1.dim() != 2:
+        raise CheckpointError(f"{src}: missing or misshapen layers.0.feed_forward.w1.weight")
+    spec = spec_from_params(params, int(w1.shape[0]), dtype)
     shapes = expected_shapes(spec)
     missing = [k for k in shapes if k not in state]
     extra = [k for k in state if k not in shapes]
@@ -147,10 +153,10 @@ def save_checkpoint(directory: str, spec: ModelSpec, tensors: dict, multiple_of:
               "n_kv_heads": spec.n_kv_heads, "vocab_size": spec.vocab_size,
               "norm_eps": spec.norm_eps, "rope_theta": spec.rope_theta}
     if multiple_of is not None:
-        if ffn_hidden_from_params(spec.dim, multiple_of, ffn_dim_multiplier) != spec.ffn_hidden:
-            raise CheckpointError("multiple_of / ffn_dim_multiplier do not give spec.ffn_hidden")
         params["multiple_of"] = multiple_of
         params["ffn_dim_multiplier"] = ffn_dim_multiplier
+        if not params_admit_ffn_width(params, spec.ffn_hidden):
+            raise CheckpointError("multiple_of / ffn_dim_multiplier do not admit spec.ffn_hidden")
     os.makedirs(directory, exist_ok=True)
     torch.save({k: tensors[k] for k in shapes}, os.path.join(directory, "consolidated.00.pth"))
     with open(os.path.join(directory, "params.json"), "w") as f:

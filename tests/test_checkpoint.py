@@ -15,25 +15,36 @@ from llama_decoder_forward_amd import synthetic as syn
 
 
 def test_params_printed_in_the_article_give_the_8b_shape():
-    # the params.json the article prints for Meta-Llama-3-8B
+    # the params.json the article prints for Meta-Llama-3-8B, with the 14336 rows of W1
     params = {"dim": 4096, "n_layers": 32, "n_heads": 32, "n_kv_heads": 8, "vocab_size": 128256,
               "multiple_of": 1024, "ffn_dim_multiplier": 1.3, "norm_eps": 1e-05,
               "rope_theta": 500000.0}
-    spec = ck.spec_from_params(params)
+    spec = ck.spec_from_params(params, 14336)
     assert spec == syn.LLAMA3_8B
 
 
 def test_stored_ffn_width_must_agree_with_params():
     params = {"dim": 4096, "n_layers": 1, "n_heads": 32, "n_kv_heads": 8, "vocab_size": 128256,
               "multiple_of": 1024, "ffn_dim_multiplier": 1.3}
-    assert ck.spec_from_params(params, ffn_hidden=14336).ffn_hidden == 14336
-    with pytest.raises(ck.CheckpointError):
-        ck.spec_from_params(params, ffn_hidden=14335)
+    assert ck.spec_from_params(params, 14336).ffn_hidden == 14336
+    # not a multiple of 1024; one block short of 14198 (rounded down); one block too many;
+    # the width without the multiplier
+    for bad in (14335, 13312, 15360, 11264, 0):
+        with pytest.raises(ck.CheckpointError):
+            ck.spec_from_params(params, bad)
+    # the same rule agrees with the oracle's FFN-width helper over many shapes
+    from oracle import llama_oracle as O
+    for dim in (64, 128, 512, 1000, 4096, 5120, 8192):
+        for mo in (32, 64, 256, 1024):
+            for mult in (None, 1.0, 1.3, 1.5):
+                w = O.ffn_hidden_size(dim, mo, mult)
+                p = {"dim": dim, "multiple_of": mo, "ffn_dim_multiplier": mult}
+                assert ck.params_admit_ffn_width(p, w)
+                assert not ck.params_admit_ffn_width(p, w + mo)
+                assert not ck.params_admit_ffn_width(p, w - mo)
     # without multiple_of the stored width is taken as is
     p2 = {k: v for k, v in params.items() if k != "multiple_of"}
-    assert ck.spec_from_params(p2, ffn_hidden=1000).ffn_hidden == 1000
-    with pytest.raises(ck.CheckpointError):
-        ck.spec_from_params(p2)
+    assert ck.spec_from_params(p2, 1000).ffn_hidden == 1000
 
 
 def _tensors(synth):

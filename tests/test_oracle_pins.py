@@ -259,6 +259,99 @@ def test_layer_matches_torch_library_composition():
     np.testing.assert_allclose(got, _torch_layer(x, W, cfg, 0), rtol=1e-11, atol=1e-12)
 
 
+# ------------------------------------------------------------------ the whole stack
+
+def _torch_stack(tokens, W, cfg):
+    """The stack from torch library routines (article, sections 分词器与编码 and
+    预测下一个输出): F.embedding of tok_embeddings, the layers in order (each from
+    _torch_layer), one F.rms_norm with norm.weight, then F.linear with output.weight.
+    Logits of every position [S, V]."""
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))  # noqa: E731
+    x = F.embedding(torch.from_numpy(np.asarray(tokens, dtype=np.int64)), t(W["tok_embeddings.weight"]))
+    for layer in range(cfg.n_layers):
+        x = torch.from_numpy(_torch_layer(x.numpy(), W, cfg, layer))
+    y = F.rms_norm(x, (cfg.dim,), t(W["norm.weight"]), eps=cfg.norm_eps)
+    return F.linear(y, t(W["output.weight"])).numpy()
+
+
+def _stack_pin_holds(seed=12):
+    cfg = syn.TINY
+    W = syn.FloatView(syn.SyntheticWeights(cfg, seed=seed))
+    toks = syn.tokens(seed, 1, 17, cfg.vocab_size)
+    got, _ = O.prefill(toks, W, cfg, all_positions=True)
+    last, _ = O.prefill(toks, W, cfg)
+    ref = _torch_stack(toks[0], W, cfg)
+    return (np.allclose(got[0], ref, rtol=1e-11, atol=1e-11)
+            and np.allclose(last[0], ref[-1], rtol=1e-11, atol=1e-11))
+
+
+def test_stack_matches_torch_library_composition():
+    # embedding, the layer loop, the final norm applied once and the untied output
+    # projection, each from an independent library routine
+    assert _stack_pin_holds()
+
+
+def test_embedding_rows_by_hand():
+    cfg = syn.TINY
+    W = syn.FloatView(syn.SyntheticWeights(cfg, seed=13))
+    toks = np.array([0, 255, 7, 7, 128])
+    x = O.embed(toks, W)
+    E = W["tok_embeddings.weight"]
+    for i, tok in enumerate(toks):
+        np.testing.assert_array_equal(x[i], E[tok])
+
+
+def _planted(monkeypatch, which):
+    """Plant one plausible mistake in the oracle (on the CPU) and report whether the stack
+    pin still holds."""
+    real_embed, real_head, real_layer = O.embed, O.head_logits, O.layer_forward
+    if which == "final norm twice":
+        def head(x, weights, cfg, bf16_points=False):
+            w = np.asarray(weights["norm.weight"], dtype=x.dtype)
+            y = O.rms_norm(O.rms_norm(x, w, cfg.norm_eps), w, cfg.norm_eps)
+            return y @ np.asarray(weights["output.weight"], dtype=x.dtype).T
+        monkeypatch.setattr(O, "head_logits", head)
+    elif which == "head tied to the embedding":
+        def head(x, weights, cfg, bf16_points=False):
+            y = O.rms_norm(x, np.asarray(weights["norm.weight"], dtype=x.dtype), cfg.norm_eps)
+            return y @ np.asarray(weights["tok_embeddings.weight"], dtype=x.dtype).T
+        monkeypatch.setattr(O, "head_logits", head)
+    elif which == "wrong embedding row":
+        monkeypatch.setattr(O, "embed", lambda tokens, weights, dtype=np.float64:
+                            real_embed((np.asarray(tokens) + 1) % 256, weights, dtype))
+    elif which == "layers in reverse order":
+        def layer(x, weights, cfg, layer, cache, start_pos, bf16_points=False):
+            return real_layer(x, weights, cfg, cfg.n_layers - 1 - layer, cache, start_pos, bf16_points)
+        monkeypatch.setattr(O, "layer_forward", layer)
+    elif which == "no final norm":
+        def head(x, weights, cfg, bf16_points=False):
+            return x @ np.asarray(weights["output.weight"], dtype=x.dtype).T
+        monkeypatch.setattr(O, "head_logits", head)
+    elif which == "last layer skipped":
+        def layer(x, weights, cfg, layer, cache, start_pos, bf16_points=False):
+            if layer == cfg.n_layers - 1:
+                return x
+            return real_layer(x, weights, cfg, layer, cache, start_pos, bf16_points)
+        monkeypatch.setattr(O, "layer_forward", layer)
+    else:
+        raise ValueError(which)
+    try:
+        return _stack_pin_holds()
+    finally:
+        monkeypatch.setattr(O, "embed", real_embed)
+        monkeypatch.setattr(O, "head_logits", real_head)
+        monkeypatch.setattr(O, "layer_forward", real_layer)
+
+
+@pytest.mark.parametrize("mistake", ["final norm twice", "head tied to the embedding",
+                                     "wrong embedding row", "layers in reverse order",
+                                     "no final norm", "last layer skipped"])
+def test_stack_pin_catches_planted_mistakes(monkeypatch, mistake):
+    assert _stack_pin_holds()
+    assert not _planted(monkeypatch, mistake), f"the stack pin missed: {mistake}"
+    assert _stack_pin_holds()
+
+
 # ------------------------------------------------------------------ cache and decode invariants
 
 def test_decode_reproduces_prefill_logits():
