@@ -167,15 +167,15 @@ def long_context(spec, weights, prefill_runs: int, decode_steps: int) -> dict:
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ml = bd.Model(spec, weights, max_batch=L_B, max_seq=L_S + decode_steps, max_tokens=L_B * L_S)
     ltoks = torch.from_numpy(syn.tokens(5, L_B, L_S, spec.vocab_size)).cuda()
-    lg = ml.prefill(ltoks)                            # warmup
+    ml.prefill(ltoks)                                 # warmup
     torch.cuda.synchronize()
     start.record(stream)
     for _ in range(prefill_runs):
-        lg = ml.prefill(ltoks)
+        ml.prefill(ltoks)
     stop.record(stream)
     torch.cuda.synchronize()
     lp_ms = start.elapsed_time(stop) / prefill_runs
-    first = lg.argmax(-1).to(torch.int32).contiguous()
+    _, first = ml.prefill(ltoks, want_next=True)      # untimed: the first greedy tokens
     ml.generate(first, L_S, decode_steps)             # warmup (same positions)
     torch.cuda.synchronize()
     start.record(stream)
@@ -328,8 +328,7 @@ def main() -> int:
     if run_decode:
         dtoks = torch.from_numpy(syn.tokens(4, dec_B, dec_ctx, spec.vocab_size)).cuda()
         t = time.perf_counter()
-        lg = m.prefill(dtoks)
-        first = lg.argmax(-1).to(torch.int32).contiguous()
+        _, first = m.prefill(dtoks, want_next=True)
         torch.cuda.synchronize()
         log(f"decode setup prefill ({dec_B} x {dec_ctx}) in {time.perf_counter() - t:.1f} s")
         m.generate(first, dec_ctx, dec_steps)            # warmup (same positions)

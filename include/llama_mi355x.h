@@ -64,7 +64,7 @@ typedef struct {
     int32_t n_layers;    /* L                                                               */
     int32_t n_heads;     /* query heads H                                                   */
     int32_t n_kv_heads;  /* key/value heads G; H % G == 0; query head h uses KV head h/(H/G) */
-    int32_t head_dim;    /* d, even, <= 256                                                  */
+    int32_t head_dim;    /* d, a multiple of 4, <= 256                                        */
     int32_t ffn_hidden;  /* SwiGLU hidden width F (14336 for the 8B shape)                   */
     int32_t vocab_size;  /* V                                                                */
     float norm_eps;      /* RMSNorm epsilon                                                  */
@@ -98,12 +98,18 @@ typedef struct {
 
 typedef struct llama_model llama_model; /* opaque handle */
 
-/* Bytes of KV cache the caller must provide for this config (layout is internal). */
+/* Bytes of KV cache the caller must provide for this config (layout is internal): keys
+ * and values of every layer for max_batch sequences of max_seq positions, the cache the
+ * Hacker News thread describes as pre-allocated by max_seq_len x max_batch_size.  0 if
+ * the config is invalid (llama_last_error says why). */
 size_t llama_kv_cache_bytes(const llama_config *cfg);
 
-/* Bytes of device workspace the caller must provide for this config (activations of up
- * to max_tokens rows, attention partials, split-K sums of the few-row GEMMs, the RoPE
- * table, device flags). */
+/* Bytes of device workspace the caller must provide for this config: the activations of
+ * up to max(max_tokens, max_batch) rows between the steps of the article's layer (sections
+ * 构建Transformer层 to 前馈神经网络层), the rotary table of section 位置编码, attention
+ * partials, split-K sums of the few-row GEMMs, device flags.  The largest call is fixed by
+ * the config's max_tokens, so the size depends on the config alone.  0 if the config is
+ * invalid. */
 size_t llama_workspace_bytes(const llama_config *cfg);
 
 /* Validate cfg, borrow the weights, KV cache and workspace, and return a handle in *out.
@@ -119,11 +125,13 @@ llama_status llama_init_weights(const llama_config *cfg, const llama_weights *we
                                 void *kv_cache, size_t kv_bytes,
                                 void *workspace, size_t ws_bytes, llama_model **out);
 
-/* Causal prefill of B independent sequences of S tokens each, starting at position 0:
- * embeds tokens [B,S], runs every layer (writing the KV cache at positions 0..S-1 of
- * sequences 0..B-1), applies the final RMSNorm and the vocabulary projection.  Writes fp32
- * logits [B,V] of each sequence's last position, or [B,S,V] of every position when
- * all_positions != 0.  Needs B <= max_batch, S <= max_seq, B*S <= max_tokens. */
+/* Causal prefill of B independent sequences of S tokens each, starting at position 0
+ * (article, sections 分词器与编码 through 预测下一个输出): embeds tokens [B,S], runs every
+ * layer (writing the KV cache at positions 0..S-1 of sequences 0..B-1), applies the final
+ * RMSNorm and the vocabulary projection.  Writes fp32 logits [B,V] of each sequence's last
+ * position, or [B,S,V] of every position when all_positions != 0.  Needs B <= max_batch,
+ * S <= max_seq, B*S <= max_tokens.  Equals llama_prefill_at with start_pos 0 and no
+ * next_tokens. */
 llama_status llama_prefill(llama_model *m, const int32_t *tokens, int32_t B, int32_t S,
                            float *logits, int32_t all_positions, hipStream_t stream);
 
@@ -132,18 +140,22 @@ llama_status llama_prefill(llama_model *m, const int32_t *tokens, int32_t B, int
  * and values are written to the cache there, and each attends causally to cache positions
  * 0..its own position, which needs the cache filled at 0..start_pos-1 by earlier calls
  * (article, section 多头注意力 for the causal mask; the cache itself is the Hacker News
- * thread's pre-allocated max_seq_len x max_batch_size buffer).  Logits as llama_prefill;
- * llama_prefill is this call with start_pos = 0.  Needs start_pos >= 0,
- * start_pos + S <= max_seq, B <= max_batch, B*S <= max_tokens; CAPACITY otherwise. */
+ * thread's pre-allocated max_seq_len x max_batch_size buffer).  Logits as llama_prefill.
+ * If next_tokens is not NULL it receives int32 [B]: the greedy choice from each sequence's
+ * last position, the argmax of its logits with the lowest index on ties (article, section
+ * 预测下一个输出).  Needs start_pos >= 0, start_pos + S <= max_seq, B <= max_batch,
+ * B*S <= max_tokens; CAPACITY otherwise. */
 llama_status llama_prefill_at(llama_model *m, const int32_t *tokens, int32_t B, int32_t S,
                               int32_t start_pos, float *logits, int32_t all_positions,
-                              hipStream_t stream);
+                              int32_t *next_tokens, hipStream_t stream);
 
 /* One KV-cache decode step: token tokens[b] of sequence b sits at position pos, its key
- * and value are written to the cache at pos, and it attends to cache positions 0..pos.
- * Writes next_tokens[b] = argmax of its logits (lowest index on ties) and, if logits is
- * not NULL, the fp32 logits [B,V].  Needs B <= max_batch, 0 <= pos < max_seq, and the
- * cache filled at 0..pos-1 by earlier calls.  tokens and next_tokens may alias. */
+ * and value are written to the cache at pos, and it attends to cache positions 0..pos
+ * (the article's layer, sections 构建Transformer层 to 前馈神经网络层, for one new token;
+ * the cache is the Hacker News thread's pre-allocated one).  Writes next_tokens[b] =
+ * argmax of its logits (lowest index on ties; article, section 预测下一个输出) and, if
+ * logits is not NULL, the fp32 logits [B,V].  Needs B <= max_batch, 0 <= pos < max_seq,
+ * and the cache filled at 0..pos-1 by earlier calls.  tokens and next_tokens may alias. */
 llama_status llama_decode_step(llama_model *m, const int32_t *tokens, int32_t B, int32_t pos,
                                float *logits, int32_t *next_tokens, hipStream_t stream);
 
@@ -159,7 +171,9 @@ llama_status llama_decode_step_ragged(llama_model *m, const int32_t *tokens, int
                                       int32_t *next_tokens, hipStream_t stream);
 
 /* n_steps greedy decode steps starting with tokens[b] at position pos: step k runs at
- * position pos+k on the previous step's argmax.  The position and step index live in
+ * position pos+k on the previous step's argmax (the article's greedy choice, section
+ * 预测下一个输出, fed back as the next token over the pre-allocated cache of the Hacker
+ * News thread).  The position and step index live in
  * device memory, so the whole loop is enqueued at once with no host synchronisation.
  * Writes out_tokens[k*B + b], the argmax of step k; if logits is not NULL also the logits
  * [n_steps,B,V].  Needs pos + n_steps <= max_seq.
@@ -185,8 +199,22 @@ llama_status llama_layer_forward(llama_model *m, int32_t layer, const float *x_i
 /* Synchronise the stream, then report device-detected input errors since the last check
  * (token ids outside [0,V) give INVALID_ARG; their embedding rows are zero; NaN logits in
  * argmax give INVALID_ARG; so do ragged-decode positions outside [0, max_seq)) and clear
- * them. */
+ * them.  The checks guard the embedding lookup (article, section 分词器与编码) and the
+ * greedy argmax (section 预测下一个输出), whose inputs the host never sees. */
 llama_status llama_sync_status(llama_model *m, hipStream_t stream);
+
+/* Record the residual stream between the article's layers (section 预测下一个输出: the
+ * embedding passes through the 32 layers in turn, then the final norm): while hidden is
+ * set, each llama_prefill / llama_prefill_at / llama_decode_step(_ragged) /
+ * llama_generate call writes, as fp32 rows of dim values, the input of every layer l to
+ * hidden[l][row] (rows = B*S in token order for prefill, B for decode; after the
+ * embedding for l = 0) and the rows the final RMSNorm reads to hidden[n_layers][row] (each
+ * sequence's last position, or every position with all_positions; B rows in decode).
+ * hidden holds (n_layers + 1) * max_rows * dim floats, 16-byte aligned, owned by the
+ * caller; a call with more rows than max_rows returns CAPACITY.  llama_generate leaves its
+ * last step.  llama_layer_forward is not recorded.  NULL stops recording.  Errors:
+ * INVALID_ARG, SHAPE (max_rows <= 0). */
+llama_status llama_trace_hidden(llama_model *m, float *hidden, int32_t max_rows);
 
 /* Kernel classes of the forward pass, for llama_profile_kernel. */
 typedef enum {

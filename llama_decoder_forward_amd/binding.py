@@ -48,8 +48,8 @@ class LlamaWeights(ctypes.Structure):
 
 
 EXPORTS = ["llama_kv_cache_bytes", "llama_workspace_bytes", "llama_init_weights", "llama_prefill",
-           "llama_prefill_at", "llama_decode_step", "llama_decode_step_ragged", "llama_generate",
-           "llama_layer_forward", "llama_sync_status", "llama_free", "llama_last_error",
+           "llama_prefill_at", "llama_decode_step", "llama_decode_step_ragged", "llama_generate", "llama_layer_forward",
+           "llama_sync_status", "llama_trace_hidden", "llama_free", "llama_last_error",
            "llama_profile_kernel", "llama_profile_read"]
 
 KERNELS = {"none": 0, "qkv": 1, "attention": 2, "wo": 3, "ffn_up": 4, "ffn_down": 5,
@@ -74,12 +74,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.llama_workspace_bytes.restype = Z
     lib.llama_init_weights.argtypes = [F(LlamaConfig), F(LlamaWeights), P, Z, P, Z, F(P)]
     lib.llama_prefill.argtypes = [P, P, I, I, P, I, P]
-    lib.llama_prefill_at.argtypes = [P, P, I, I, I, P, I, P]
+    lib.llama_prefill_at.argtypes = [P, P, I, I, I, P, I, P, P]
     lib.llama_decode_step.argtypes = [P, P, I, I, P, P, P]
     lib.llama_decode_step_ragged.argtypes = [P, P, I, P, P, P, P]
     lib.llama_generate.argtypes = [P, P, I, I, I, P, P, P]
     lib.llama_layer_forward.argtypes = [P, I, P, P, I, I, I, P]
     lib.llama_sync_status.argtypes = [P, P]
+    lib.llama_trace_hidden.argtypes = [P, P, I]
     lib.llama_profile_kernel.argtypes = [P, ctypes.c_int]
     lib.llama_profile_read.argtypes = [P, F(ctypes.c_double), F(ctypes.c_int32)]
     lib.llama_free.argtypes = [P]
@@ -87,8 +88,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.llama_last_error.argtypes = []
     lib.llama_last_error.restype = ctypes.c_char_p
     for fn in ("llama_init_weights", "llama_prefill", "llama_prefill_at", "llama_decode_step",
-               "llama_decode_step_ragged", "llama_generate", "llama_layer_forward",
-               "llama_sync_status", "llama_profile_kernel", "llama_profile_read"):
+               "llama_decode_step_ragged", "llama_generate",
+               "llama_layer_forward", "llama_sync_status", "llama_trace_hidden",
+               "llama_profile_kernel", "llama_profile_read"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -165,21 +167,24 @@ class Model:
 
     # -------------------------------------------------------------- calls
     def prefill(self, tokens: torch.Tensor, all_positions: bool = False, logits=None, stream=None,
-                start_pos: int = 0):
-        """Prefill [B, S] tokens at positions start_pos.. (llama_prefill / llama_prefill_at)."""
+                start_pos: int = 0, want_next: bool = False):
+        """Prefill [B, S] tokens at positions start_pos.. (llama_prefill / llama_prefill_at).
+        Returns the logits, or (logits, next tokens [B]) with want_next."""
         B, S = tokens.shape
         assert tokens.dtype == torch.int32 and tokens.is_contiguous()
         V = self.spec.vocab_size
         if logits is None:
             shape = (B, S, V) if all_positions else (B, V)
             logits = torch.empty(shape, dtype=torch.float32, device=self.device)
-        if start_pos == 0:
+        nxt = torch.empty(B, dtype=torch.int32, device=self.device) if want_next else None
+        if start_pos == 0 and not want_next:
             check(self.lib.llama_prefill(self.handle, _ptr(tokens), B, S, _ptr(logits),
                                          int(all_positions), _stream(stream)))
         else:
             check(self.lib.llama_prefill_at(self.handle, _ptr(tokens), B, S, start_pos,
-                                            _ptr(logits), int(all_positions), _stream(stream)))
-        return logits
+                                            _ptr(logits), int(all_positions), _ptr(nxt),
+                                            _stream(stream)))
+        return (logits, nxt) if want_next else logits
 
     def decode_step(self, tokens: torch.Tensor, pos: int, want_logits: bool = True,
                     next_tokens=None, logits=None, stream=None):
@@ -193,6 +198,19 @@ class Model:
                                          _ptr(logits) if want_logits else None,
                                          _ptr(next_tokens), _stream(stream)))
         return next_tokens, (logits if want_logits else None)
+
+    def trace_hidden(self, max_rows: int | None):
+        """Record the residual stream of later calls (llama_trace_hidden) into a new tensor
+        [n_layers + 1, max_rows, dim], returned; None stops recording."""
+        if max_rows is None:
+            check(self.lib.llama_trace_hidden(self.handle, None, 0))
+            self._trace = None
+            return None
+        buf = torch.zeros((self.spec.n_layers + 1, max_rows, self.spec.dim), dtype=torch.float32,
+                          device=self.device)
+        check(self.lib.llama_trace_hidden(self.handle, _ptr(buf), max_rows))
+        self._trace = buf  # keep it alive while recorded into
+        return buf
 
     def decode_step_ragged(self, tokens: torch.Tensor, positions: torch.Tensor,
                            want_logits: bool = True, next_tokens=None, logits=None, stream=None):

@@ -36,13 +36,10 @@ struct Layout {
     size_t flags, rope, x, h, q, attn, g, logits, partials, kpart, tokbuf, argmax, total;
 };
 
-constexpr int kDecodeChunk = 64;  // key positions per split of the decode attention
-
 Layout layout_of(const llama_config& c) {
     const size_t es = elem_size(c);
     const size_t rows = (size_t)std::max(c.max_tokens, c.max_batch);
     const size_t D = c.dim, HD = (size_t)c.n_heads * c.head_dim;
-    const size_t splits = (size_t)seq_stride_of(c) / kDecodeChunk;
     Layout L{};
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
@@ -56,7 +53,7 @@ Layout layout_of(const llama_config& c) {
     L.attn = take(arows * HD * es);
     L.g = take(arows * (size_t)c.ffn_hidden * es);
     L.logits = take((size_t)c.max_batch * c.vocab_size * 4);
-    L.partials = take((size_t)c.max_batch * c.n_heads * splits * (c.head_dim + 2) * 4);
+    L.partials = take(lk::decode_partials_bytes(c.max_batch, c.n_heads, c.head_dim, seq_stride_of(c)));
     // split-K sums of the residual GEMMs on the few-row path (at most 64 rows)
     L.kpart = take((size_t)lk::LLAMA_MAX_KSPLITS * 64 * D * 4);
     L.tokbuf = take((size_t)c.max_batch * 4);
@@ -109,6 +106,9 @@ struct llama_model {
     size_t es = 2;
     int seq_stride = 0;
     bool rope_ready = false;
+    // residual-stream trace (llama_trace_hidden): [n_layers + 1][trace_rows][dim] or NULL
+    float* trace = nullptr;
+    int trace_rows = 0;
     // kernel timing (llama_profile_kernel)
     int prof_kind = LLAMA_KERNEL_NONE;
     std::vector<hipEvent_t> prof_events;  // pairs: start, stop
@@ -128,6 +128,9 @@ struct llama_model {
     float* kpart() { return reinterpret_cast<float*>(ws + L.kpart); }
     int* tokbuf() { return reinterpret_cast<int*>(ws + L.tokbuf); }
     void* argmax_scratch() { return ws + L.argmax; }
+    float* trace_slot(int l) {
+        return trace ? trace + (size_t)l * trace_rows * cfg.dim : nullptr;
+    }
     size_t kv_layer_elems() const {
         return (size_t)cfg.max_batch * cfg.n_kv_heads * seq_stride * cfg.head_dim;
     }
@@ -149,6 +152,14 @@ namespace {
 // or written by a layer) those positions add exactly 0 * V.
 llama_status ensure_rope(llama_model* m, hipStream_t s) {
     if (m->rope_ready) return LLAMA_OK;
+    // the set-up must run, not only be recorded: a graph made of it would leave every later
+    // eager call without a rotary table or a cleared cache
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(s, &cs));
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(LLAMA_ERR_INVALID_ARG,
+                    "the first call on a model runs its one-time set-up and cannot be recorded "
+                    "into a stream capture; make one call outside the capture first");
     HIP_TRY(lk::zero_u32(m->deverr(), 64, s));  // device flags and counters (first 256 bytes)
     HIP_TRY(lk::rope_table(m->rope(), m->cfg.max_seq, m->cfg.head_dim, m->cfg.rope_theta, s));
     HIP_TRY(lk::zero_bytes(m->kv, llama_kv_cache_bytes(&m->cfg), s));
@@ -206,12 +217,26 @@ struct Pending {
     size_t stride = 0;
 };
 
+// Scratch of one call: split-K sums of the few-row residual GEMMs, decode-attention split
+// partials, argmax partials and the logits of a decode step whose caller wants none.  The
+// model's workspace holds them (Scratch::of).
+struct Scratch {
+    float* kpart;
+    float* partials;
+    void* argmax;
+    float* logits;
+    static Scratch of(llama_model* m) {
+        return Scratch{m->kpart(), m->partials(), m->argmax_scratch(), m->logits_scratch()};
+    }
+};
+
 // One decoder layer on rows = B*S tokens (article, sections 构建Transformer层 to 前馈神经网络层).
 // pend, if given: on entry the sums pending on xin (then xin is written, folded), on return
 // those pending on xout.  Without it xout is complete on return.
+// trace: if set, receives the layer's input rows (after pending sums are added).
 llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int B, int S,
                        int start_pos, const int* pos_dev, int pos_stride, int max_ctx, bool decode,
-                       Pending* pend, hipStream_t s) {
+                       Pending* pend, const Scratch& scr, float* trace, hipStream_t s) {
     const llama_config& c = m->cfg;
     const llama_layer_weights& w = m->layers[l];
     const int T = B * S, D = c.dim, H = c.n_heads, G = c.n_kv_heads, d = c.head_dim;
@@ -226,10 +251,11 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
         ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
         const Pending in = pend ? *pend : Pending{};
         // pending sums exist only on the library's own residual buffer, which is writable
-        HIP_TRY(lk::rmsnorm_fold(m->dt, xin, m->kpart(), in.splits, in.stride,
+        HIP_TRY(lk::rmsnorm_fold(m->dt, xin, scr.kpart, in.splits, in.stride,
                                  const_cast<float*>(xin), 1, 0, w.attention_norm, m->h(), pk_qkv,
                                  T, D, c.norm_eps, s));
     }
+    if (trace) HIP_TRY(lk::copy_rows(xin, 1, 0, trace, T, D, s));
 
     lk::GemmArgs<void> qkv = gemm_args(m, m->h(), D, w.wq, T, Nq + 2 * Nk, D);
     qkv.W = WeightRows<void>{w.wq, w.wk, w.wv, Nq, Nq + Nk, D};
@@ -241,7 +267,7 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
     }
 
     lk::AttnArgs aa{m->q(), m->kc(l), m->vc(l), m->attn(), pk_wo, B, S, start_pos, H, G, d,
-                    m->seq_stride, pos_dev, pos_stride, c.max_seq, m->partials(), max_ctx};
+                    m->seq_stride, pos_dev, pos_stride, c.max_seq, scr.partials, max_ctx};
     {
         ProfScope ps(m, LLAMA_KERNEL_ATTENTION, s);
         if (decode) HIP_TRY(lk::attention_decode(m->dt, aa, s));
@@ -252,13 +278,13 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
     {
         ProfScope ps(m, LLAMA_KERNEL_WO, s);
         const lk::GemmArgs<void> ga = gemm_args(m, m->attn(), Nq, w.wo, T, D, Nq);
-        if (wo_splits > 0) HIP_TRY(lk::gemm_residual_split(m->dt, ga, m->kpart(), wo_splits, s));
+        if (wo_splits > 0) HIP_TRY(lk::gemm_residual_split(m->dt, ga, scr.kpart, wo_splits, s));
         else HIP_TRY(lk::gemm_residual(m->dt, ga, EpiResidual{xin, xout, D}, s));
     }
     {
         ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
         if (wo_splits > 0)
-            HIP_TRY(lk::rmsnorm_fold(m->dt, xin, m->kpart(), wo_splits, (size_t)T * D, xout, 1, 0,
+            HIP_TRY(lk::rmsnorm_fold(m->dt, xin, scr.kpart, wo_splits, (size_t)T * D, xout, 1, 0,
                                      w.ffn_norm, m->h(), pk_up, T, D, c.norm_eps, s));
         else
             HIP_TRY(lk::rmsnorm(m->dt, xout, 1, 0, w.ffn_norm, m->h(), pk_up, T, D, c.norm_eps, s));
@@ -274,7 +300,7 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
     {
         ProfScope ps(m, LLAMA_KERNEL_FFN_DOWN, s);
         const lk::GemmArgs<void> ga = gemm_args(m, m->g(), c.ffn_hidden, w.w2, T, D, c.ffn_hidden);
-        if (w2_splits > 0) HIP_TRY(lk::gemm_residual_split(m->dt, ga, m->kpart(), w2_splits, s));
+        if (w2_splits > 0) HIP_TRY(lk::gemm_residual_split(m->dt, ga, scr.kpart, w2_splits, s));
         else HIP_TRY(lk::gemm_residual(m->dt, ga, EpiResidual{xout, xout, D}, s));
     }
     if (pend) *pend = Pending{w2_splits, (size_t)T * D};
@@ -283,17 +309,20 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
 
 // Final RMSNorm and vocabulary projection of `rows` rows of x taken every `step` rows
 // starting at `offset` (article, section 预测下一个输出).
-// `pend`: split-K sums still pending on x (added to the rows read).
+// `pend`: split-K sums still pending on x (added to the rows read).  With a trace, the rows
+// read (after the pending sums) go to the last trace slot.
 llama_status run_head(llama_model* m, int rows, int step, int offset, const Pending& pend,
-                      float* logits, hipStream_t s) {
+                      const Scratch& scr, float* logits, hipStream_t s) {
     const llama_config& c = m->cfg;
     {
         ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
-        HIP_TRY(lk::rmsnorm_fold(m->dt, m->x(), m->kpart(), pend.splits, pend.stride, m->x(), step,
+        HIP_TRY(lk::rmsnorm_fold(m->dt, m->x(), scr.kpart, pend.splits, pend.stride, m->x(), step,
                                  offset, m->norm, m->h(),
                                  lk::act_pack(m->dt, rows, c.vocab_size, c.dim), rows, c.dim,
                                  c.norm_eps, s));
     }
+    if (m->trace)
+        HIP_TRY(lk::copy_rows(m->x(), step, offset, m->trace_slot(c.n_layers), rows, c.dim, s));
     {
         ProfScope ps(m, LLAMA_KERNEL_LM_HEAD, s);
         HIP_TRY(lk::gemm_store_f32(m->dt, gemm_args(m, m->h(), c.dim, m->output, rows, c.vocab_size, c.dim),
@@ -305,20 +334,20 @@ llama_status run_head(llama_model* m, int rows, int step, int offset, const Pend
 // One decode step of B rows; position from `pos` or, if pos_dev is set, from device memory.
 llama_status run_decode_step(llama_model* m, const int32_t* tokens, int B, int pos,
                              const int* pos_dev, int pos_stride, int max_ctx, float* logits,
-                             int32_t* next,
-                             int32_t* log_out, const int* step_ctr, hipStream_t s) {
+                             int32_t* next, int32_t* log_out, const int* step_ctr,
+                             const Scratch& scr, hipStream_t s) {
     const llama_config& c = m->cfg;
     HIP_TRY(lk::embed(m->dt, tokens, m->tok_embeddings, m->x(), B, c.dim, c.vocab_size, m->deverr(), s));
     Pending pend;
     for (int l = 0; l < c.n_layers; ++l) {
         llama_status st = run_layer(m, l, m->x(), m->x(), B, 1, pos, pos_dev, pos_stride, max_ctx,
-                                    true, &pend, s);
+                                    true, &pend, scr, m->trace_slot(l), s);
         if (st != LLAMA_OK) return st;
     }
-    float* lg = logits ? logits : m->logits_scratch();
-    llama_status st = run_head(m, B, 1, 0, pend, lg, s);
+    float* lg = logits ? logits : scr.logits;
+    llama_status st = run_head(m, B, 1, 0, pend, scr, lg, s);
     if (st != LLAMA_OK) return st;
-    HIP_TRY(lk::argmax(lg, B, c.vocab_size, next, log_out, B, step_ctr, m->argmax_scratch(),
+    HIP_TRY(lk::argmax(lg, B, 1, 0, c.vocab_size, next, log_out, B, step_ctr, scr.argmax,
                        m->deverr(), s));
     return LLAMA_OK;
 }
@@ -384,7 +413,7 @@ llama_status llama_init_weights(const llama_config* cfg, const llama_weights* w,
 
 llama_status llama_prefill_at(llama_model* m, const int32_t* tokens, int32_t B, int32_t S,
                               int32_t start_pos, float* logits, int32_t all_positions,
-                              hipStream_t s) {
+                              int32_t* next_tokens, hipStream_t s) {
     if (!m || !tokens || !logits) return fail(LLAMA_ERR_INVALID_ARG, "NULL model, tokens or logits");
     const llama_config& c = m->cfg;
     if (B <= 0 || S <= 0) return fail(LLAMA_ERR_SHAPE, "B and S must be positive (B=%d S=%d)", B, S);
@@ -393,23 +422,31 @@ llama_status llama_prefill_at(llama_model* m, const int32_t* tokens, int32_t B, 
         return fail(LLAMA_ERR_CAPACITY, "start_pos=%d + S=%d exceeds max_seq=%d", start_pos, S, c.max_seq);
     if ((long long)B * S > c.max_tokens)
         return fail(LLAMA_ERR_CAPACITY, "B*S=%lld > max_tokens=%d", (long long)B * S, c.max_tokens);
+    if (m->trace && (long long)B * S > m->trace_rows)
+        return fail(LLAMA_ERR_CAPACITY, "B*S=%lld > the trace's %d rows", (long long)B * S, m->trace_rows);
     llama_status st = ensure_rope(m, s);
     if (st != LLAMA_OK) return st;
     const int T = B * S;
+    const Scratch scr = Scratch::of(m);
     HIP_TRY(lk::embed(m->dt, tokens, m->tok_embeddings, m->x(), T, c.dim, c.vocab_size, m->deverr(), s));
     Pending pend;
     for (int l = 0; l < c.n_layers; ++l) {
         st = run_layer(m, l, m->x(), m->x(), B, S, start_pos, nullptr, 0, start_pos + S, false,
-                       &pend, s);
+                       &pend, scr, m->trace_slot(l), s);
         if (st != LLAMA_OK) return st;
     }
-    if (all_positions) return run_head(m, T, 1, 0, pend, logits, s);
-    return run_head(m, B, S, S - 1, pend, logits, s);
+    st = all_positions ? run_head(m, T, 1, 0, pend, scr, logits, s)
+                       : run_head(m, B, S, S - 1, pend, scr, logits, s);
+    if (st != LLAMA_OK || !next_tokens) return st;
+    // greedy choice of each sequence's last position (article, section 预测下一个输出)
+    HIP_TRY(lk::argmax(logits, B, all_positions ? S : 1, all_positions ? S - 1 : 0, c.vocab_size,
+                       next_tokens, nullptr, 0, nullptr, scr.argmax, m->deverr(), s));
+    return LLAMA_OK;
 }
 
 llama_status llama_prefill(llama_model* m, const int32_t* tokens, int32_t B, int32_t S,
                            float* logits, int32_t all_positions, hipStream_t s) {
-    return llama_prefill_at(m, tokens, B, S, 0, logits, all_positions, s);
+    return llama_prefill_at(m, tokens, B, S, 0, logits, all_positions, nullptr, s);
 }
 
 llama_status llama_decode_step(llama_model* m, const int32_t* tokens, int32_t B, int32_t pos,
@@ -419,10 +456,12 @@ llama_status llama_decode_step(llama_model* m, const int32_t* tokens, int32_t B,
     if (B <= 0) return fail(LLAMA_ERR_SHAPE, "B must be positive (B=%d)", B);
     if (B > c.max_batch) return fail(LLAMA_ERR_CAPACITY, "B=%d > max_batch=%d", B, c.max_batch);
     if (pos < 0 || pos >= c.max_seq) return fail(LLAMA_ERR_CAPACITY, "pos=%d outside [0, max_seq=%d)", pos, c.max_seq);
+    if (m->trace && B > m->trace_rows)
+        return fail(LLAMA_ERR_CAPACITY, "B=%d > the trace's %d rows", B, m->trace_rows);
     llama_status st = ensure_rope(m, s);
     if (st != LLAMA_OK) return st;
     return run_decode_step(m, tokens, B, pos, nullptr, 0, pos + 1, logits, next_tokens, nullptr,
-                           nullptr, s);
+                           nullptr, Scratch::of(m), s);
 }
 
 llama_status llama_decode_step_ragged(llama_model* m, const int32_t* tokens, int32_t B,
@@ -433,13 +472,15 @@ llama_status llama_decode_step_ragged(llama_model* m, const int32_t* tokens, int
     const llama_config& c = m->cfg;
     if (B <= 0) return fail(LLAMA_ERR_SHAPE, "B must be positive (B=%d)", B);
     if (B > c.max_batch) return fail(LLAMA_ERR_CAPACITY, "B=%d > max_batch=%d", B, c.max_batch);
+    if (m->trace && B > m->trace_rows)
+        return fail(LLAMA_ERR_CAPACITY, "B=%d > the trace's %d rows", B, m->trace_rows);
     llama_status st = ensure_rope(m, s);
     if (st != LLAMA_OK) return st;
     // positions live on the device: checked there (flag for llama_sync_status), and every
     // kernel replaces an out-of-range one by 0, so that no access leaves the cache
     HIP_TRY(lk::check_positions(positions, B, c.max_seq, m->deverr(), s));
     return run_decode_step(m, tokens, B, 0, positions, 1, c.max_seq, logits, next_tokens, nullptr,
-                           nullptr, s);
+                           nullptr, Scratch::of(m), s);
 }
 
 llama_status llama_generate(llama_model* m, const int32_t* tokens, int32_t B, int32_t pos,
@@ -451,6 +492,8 @@ llama_status llama_generate(llama_model* m, const int32_t* tokens, int32_t B, in
     if (pos < 0 || (long long)pos + n_steps > c.max_seq)
         return fail(LLAMA_ERR_CAPACITY, "pos=%d + n_steps=%d exceeds max_seq=%d", pos, n_steps, c.max_seq);
     if (n_steps == 0) return LLAMA_OK;
+    if (m->trace && B > m->trace_rows)
+        return fail(LLAMA_ERR_CAPACITY, "B=%d > the trace's %d rows", B, m->trace_rows);
     llama_status st = ensure_rope(m, s);
     if (st != LLAMA_OK) return st;
     const int max_ctx = pos + n_steps;
@@ -461,7 +504,7 @@ llama_status llama_generate(llama_model* m, const int32_t* tokens, int32_t B, in
     for (int k = 0; k < n_steps; ++k) {
         st = run_decode_step(m, m->tokbuf(), B, 0, m->pos_ctr(), 0, max_ctx,
                              logits ? logits + (size_t)k * B * c.vocab_size : nullptr,
-                             m->tokbuf(), out_tokens, m->step_ctr(), s);
+                             m->tokbuf(), out_tokens, m->step_ctr(), Scratch::of(m), s);
         if (st != LLAMA_OK) return st;
         HIP_TRY(lk::bump_counters(m->pos_ctr(), m->step_ctr(), s));
     }
@@ -483,7 +526,17 @@ llama_status llama_layer_forward(llama_model* m, int32_t layer, const float* x_i
     llama_status st = ensure_rope(m, s);
     if (st != LLAMA_OK) return st;
     return run_layer(m, layer, x_in, x_out, B, S, start_pos, nullptr, 0, start_pos + S, false,
-                     nullptr, s);
+                     nullptr, Scratch::of(m), nullptr, s);
+}
+
+llama_status llama_trace_hidden(llama_model* m, float* hidden, int32_t max_rows) {
+    if (!m) return fail(LLAMA_ERR_INVALID_ARG, "NULL model");
+    if (hidden && max_rows <= 0) return fail(LLAMA_ERR_SHAPE, "max_rows must be positive");
+    if (hidden && ((uintptr_t)hidden % 16))
+        return fail(LLAMA_ERR_INVALID_ARG, "hidden must be 16-byte aligned");
+    m->trace = hidden;
+    m->trace_rows = hidden ? max_rows : 0;
+    return LLAMA_OK;
 }
 
 llama_status llama_sync_status(llama_model* m, hipStream_t s) {

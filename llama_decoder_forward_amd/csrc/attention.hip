@@ -588,9 +588,12 @@ DecodeGrid decode_grid(const AttnArgs& a) {
     return {4, chunk, (a.max_ctx + chunk - 1) / chunk};
 }
 
+// splits a decode partial slot is sized for: the most a context of seq_stride positions takes
+int decode_max_splits(int seq_stride) { return (seq_stride + 4 * DEC_BLOCK - 1) / (4 * DEC_BLOCK); }
+
 hipError_t launch_decode_mfma(const AttnArgs& a, hipStream_t s) {
     const DecodeGrid dg = decode_grid(a);
-    const int max_splits = (a.seq_stride + 4 * DEC_BLOCK - 1) / (4 * DEC_BLOCK);
+    const int max_splits = decode_max_splits(a.seq_stride);
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_D);
     const dim3 grid(dg.splits, a.G, a.B);
     if (dg.waves == 8)
@@ -623,6 +626,10 @@ hipError_t attention_prefill(Dt dt, const AttnArgs& a, hipStream_t s) {
     if (dt == Dt::BF16 && mfma_path(a)) return launch_prefill_mfma(a, s);
     if (dt == Dt::BF16) return launch_generic<bf16>(a, s);
     return launch_generic<float>(a, s);
+}
+
+size_t decode_partials_bytes(int B, int H, int d, int seq_stride) {
+    return (size_t)B * H * decode_max_splits(seq_stride) * (d + 2) * sizeof(float);
 }
 
 hipError_t attention_decode(Dt dt, const AttnArgs& a, hipStream_t s) {

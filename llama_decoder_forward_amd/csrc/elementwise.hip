@@ -236,10 +236,11 @@ __device__ __forceinline__ void better(float& best, int& idx, float v, int i) {
 }
 
 __global__ __launch_bounds__(256) void argmax_partial_kernel(const float* logits, int V,
+                                                             int row_step, int row_off,
                                                              float* pv, int* pi, int nchunks,
                                                              uint32_t* err) {
     const int c = blockIdx.x, r = blockIdx.y;
-    const float* lr = logits + (size_t)r * V;
+    const float* lr = logits + ((size_t)r * row_step + row_off) * V;
     const int lo = c * ARGMAX_CHUNK, hi = min(V, lo + ARGMAX_CHUNK);
     float best = -INFINITY;
     int idx = 0x7fffffff;
@@ -295,13 +296,15 @@ size_t argmax_scratch_bytes(int rows, int V) {
     return (size_t)rows * nchunks * 8;
 }
 
-hipError_t argmax(const float* logits, int rows, int V, int* out, int* out2, int out2_step,
-                  const int* counter, void* scratch, uint32_t* err, hipStream_t s) {
+hipError_t argmax(const float* logits, int rows, int row_step, int row_off, int V, int* out,
+                  int* out2, int out2_step, const int* counter, void* scratch, uint32_t* err,
+                  hipStream_t s) {
     if (rows == 0) return hipSuccess;
     const int nchunks = (V + ARGMAX_CHUNK - 1) / ARGMAX_CHUNK;
     float* pv = static_cast<float*>(scratch);
     int* pi = reinterpret_cast<int*>(pv + (size_t)rows * nchunks);
-    argmax_partial_kernel<<<dim3(nchunks, rows), 256, 0, s>>>(logits, V, pv, pi, nchunks, err);
+    argmax_partial_kernel<<<dim3(nchunks, rows), 256, 0, s>>>(logits, V, row_step, row_off, pv,
+                                                              pi, nchunks, err);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     argmax_final_kernel<<<rows, 64, 0, s>>>(pv, pi, nchunks, out, out2, out2_step, counter);
@@ -353,6 +356,21 @@ __global__ void check_positions_kernel(const int* pos, int B, int max_pos, uint3
 }
 hipError_t check_positions(const int* pos, int B, int max_pos, uint32_t* err, hipStream_t s) {
     check_positions_kernel<<<(B + 255) / 256, 256, 0, s>>>(pos, B, max_pos, err);
+    return hipGetLastError();
+}
+
+// dst[r][0..D) = src[r * step + off][0..D) for r < rows (fp32 rows, D % 4 == 0)
+__global__ __launch_bounds__(256) void copy_rows_kernel(const float* src, int step, int off,
+                                                        float* dst, int D) {
+    const size_t r = blockIdx.x;
+    const f32x4* in = reinterpret_cast<const f32x4*>(src + (r * step + off) * D);
+    f32x4* out = reinterpret_cast<f32x4*>(dst + r * D);
+    for (int i = threadIdx.x; i < D / 4; i += blockDim.x) out[i] = in[i];
+}
+hipError_t copy_rows(const float* src, int step, int off, float* dst, int rows, int D,
+                     hipStream_t s) {
+    if (rows == 0) return hipSuccess;
+    copy_rows_kernel<<<rows, 256, 0, s>>>(src, step, off, dst, D);
     return hipGetLastError();
 }
 

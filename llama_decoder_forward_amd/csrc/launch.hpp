@@ -22,8 +22,13 @@ hipError_t rmsnorm_fold(Dt dt, const float* x, const float* parts, int nsplit, s
                         float* x_out, int in_row_step, int in_row_offset, const void* w, void* y,
                         int y_pack, int rows, int D, float eps, hipStream_t s);
 size_t argmax_scratch_bytes(int rows, int V);
-hipError_t argmax(const float* logits, int rows, int V, int* out, int* out2, int out2_step,
-                  const int* counter, void* scratch, uint32_t* err, hipStream_t s);
+// out[r] = argmax of logits row r * row_step + row_off, r < rows (and the token log out2)
+hipError_t argmax(const float* logits, int rows, int row_step, int row_off, int V, int* out,
+                  int* out2, int out2_step, const int* counter, void* scratch, uint32_t* err,
+                  hipStream_t s);
+// dst[r] = src[r * step + off], rows of D floats (D % 4 == 0)
+hipError_t copy_rows(const float* src, int step, int off, float* dst, int rows, int D,
+                     hipStream_t s);
 hipError_t bump_counters(int* pos, int* step, hipStream_t s);
 hipError_t zero_u32(uint32_t* p, int n, hipStream_t s);
 // fill `bytes` bytes (a multiple of 16, 16-byte aligned) with zeros
@@ -73,5 +78,7 @@ struct AttnArgs {
 };
 hipError_t attention_prefill(Dt dt, const AttnArgs& a, hipStream_t s);
 hipError_t attention_decode(Dt dt, const AttnArgs& a, hipStream_t s);
+// bytes of decode split partials (AttnArgs::partials) for B sequences of H heads
+size_t decode_partials_bytes(int B, int H, int d, int seq_stride);
 
 }  // namespace lk

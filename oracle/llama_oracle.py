@@ -68,10 +68,12 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     bfloat16 keeps the top 16 bits of a float32; rounding adds 0x7FFF plus the lowest kept
     bit before truncating.  Done on a float32 view; NaN/Inf are not expected here.
     """
-    f = np.asarray(x, dtype=np.float32)
-    u = f.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
-    return u.astype(np.uint32).view(np.float32).astype(np.asarray(x).dtype)
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32)
+    # finite inputs: the sum stays below 2**32 (the largest finite bit pattern is 0x7F7FFFFF
+    # or 0xFF7FFFFF, and at most 0x8000 is added)
+    r = (u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32).astype(np.asarray(x).dtype)
 
 
 def _maybe_bf16(x: np.ndarray, on: bool) -> np.ndarray:

@@ -124,11 +124,11 @@ def test_call_shape_and_capacity_errors_before_device_work(lib, handle):
     assert lib.llama_layer_forward(handle, 2, T, T, 1, 4, 0, None) == -1  # layer out of range
     assert lib.llama_layer_forward(handle, 0, T, T, 1, 4, 30, None) == -3
     assert lib.llama_layer_forward(handle, 0, T, T, 3, 1, 0, None) == -3
-    assert lib.llama_prefill_at(handle, T, 1, 4, 29, T, 0, None) == -3  # 29 + 4 > max_seq
-    assert lib.llama_prefill_at(handle, T, 1, 4, -1, T, 0, None) == -3
-    assert lib.llama_prefill_at(handle, T, 3, 4, 0, T, 0, None) == -3    # B > max_batch
-    assert lib.llama_prefill_at(handle, T, 1, 0, 4, T, 0, None) == -2
-    assert lib.llama_prefill_at(handle, T, 1, 4, 4, None, 0, None) == -1
+    assert lib.llama_prefill_at(handle, T, 1, 4, 29, T, 0, None, None) == -3  # 29 + 4 > max_seq
+    assert lib.llama_prefill_at(handle, T, 1, 4, -1, T, 0, None, None) == -3
+    assert lib.llama_prefill_at(handle, T, 3, 4, 0, T, 0, None, None) == -3    # B > max_batch
+    assert lib.llama_prefill_at(handle, T, 1, 0, 4, T, 0, None, None) == -2
+    assert lib.llama_prefill_at(handle, T, 1, 4, 4, None, 0, None, None) == -1
     assert lib.llama_decode_step_ragged(handle, T, 3, T, T, T, None) == -3  # B > max_batch
     assert lib.llama_decode_step_ragged(handle, T, 0, T, T, T, None) == -2
     assert lib.llama_decode_step_ragged(handle, T, 1, None, T, T, None) == -1
@@ -137,6 +137,23 @@ def test_call_shape_and_capacity_errors_before_device_work(lib, handle):
     assert lib.llama_decode_step(handle, T, 3, 3, T, T, None) == -3
     assert "max_batch" in lib.llama_last_error().decode()
     assert lib.llama_sync_status(None, None) == -1
+
+
+def test_trace_validation_before_device_work(lib, handle):
+    T = 0x300000
+    assert lib.llama_trace_hidden(None, T, 4) == -1
+    assert lib.llama_trace_hidden(handle, T, 0) == -2
+    assert lib.llama_trace_hidden(handle, T + 4, 4) == -1          # not 16-byte aligned
+    assert lib.llama_trace_hidden(handle, T, 4) == 0
+    # calls with more rows than the trace holds fail before any launch
+    assert lib.llama_prefill(handle, T, 1, 5, T, 0, None) == -3
+    assert "trace" in lib.llama_last_error().decode()
+    assert lib.llama_prefill_at(handle, T, 2, 3, 0, T, 0, None, None) == -3
+    assert lib.llama_trace_hidden(handle, T, 1) == 0
+    assert lib.llama_decode_step(handle, T, 2, 3, T, T, None) == -3
+    assert lib.llama_decode_step_ragged(handle, T, 2, T, T, T, None) == -3
+    assert lib.llama_generate(handle, T, 2, 3, 2, T, None, None) == -3
+    assert lib.llama_trace_hidden(handle, None, 0) == 0              # stop recording
 
 
 def test_max_tokens_bounds_prefill(lib):

@@ -71,7 +71,9 @@ def test_decode_8b_widths(B, ctx, rows, steps):
     spec = _spec(1)
     m, synth = build_model(spec, 4, max_batch=B, max_seq=ctx + steps, max_tokens=B * ctx, cache=False)
     toks = syn.tokens(4, B, ctx, spec.vocab_size)
-    got0 = m.prefill(torch.from_numpy(toks).cuda()).cpu().numpy()
+    got0, first = m.prefill(torch.from_numpy(toks).cuda(), want_next=True)
+    got0 = got0.cpu().numpy()
+    np.testing.assert_array_equal(first.cpu().numpy(), np.argmax(got0, axis=-1))
     W = _oracle_weights(synth, 1)
     say("  oracle prefill of the checked rows (float32)")
     sub = toks[list(rows)]
@@ -79,19 +81,43 @@ def test_decode_8b_widths(B, ctx, rows, steps):
     assert_rows_close(got0[list(rows)], ref0, BF16_TOL, "prefill logits")
     # teacher forcing: every row is fed the oracle's choice for the checked rows and the
     # GPU's own choice for the others
-    cur_all = np.argmax(got0, axis=-1).astype(np.int32)
+    cur_all = first.cpu().numpy().astype(np.int32)
     cur_ref = O.argmax(ref0).astype(np.int32)
+    first_tf = cur_all.copy()
+    first_tf[list(rows)] = cur_ref
+    ref_step0 = None
     for k in range(steps):
         cur_all[list(rows)] = cur_ref
         nxt, lg = m.decode_step(torch.from_numpy(cur_all).cuda(), ctx + k)
         lg = lg.cpu().numpy()
         nxt = nxt.cpu().numpy()
         ref = O.decode_step(cur_ref, ctx + k, W, spec, caches, dtype=np.float32)
+        ref_step0 = ref if k == 0 else ref_step0
         assert_rows_close(lg[list(rows)], ref, BF16_TOL, f"decode step {k}")
         check_argmax(nxt[list(rows)], lg[list(rows)], ref, f"decode step {k}")
         np.testing.assert_array_equal(nxt, np.argmax(lg, axis=-1))
         cur_ref = O.argmax(ref).astype(np.int32)
         cur_all = nxt.astype(np.int32)
+    if B == 32:
+        # the benchmarked loop: llama_generate (position and step in device memory, the
+        # argmax fed back on the device) against eager llama_decode_step calls from the same
+        # tokens, bit for bit; its first step against the oracle on the checked rows
+        say("  llama_generate vs eager decode steps")
+        start = torch.from_numpy(first_tf).cuda()
+        eager_tok, eager_lg = [], []
+        cur = start
+        for k in range(steps):
+            cur, lg = m.decode_step(cur, ctx + k)
+            eager_tok.append(cur.clone())
+            eager_lg.append(lg.clone())
+        gen_tok, gen_lg = m.generate(start, ctx, steps, want_logits=True)
+        assert torch.equal(gen_tok, torch.stack(eager_tok)), "generate tokens != eager"
+        assert torch.equal(gen_lg, torch.stack(eager_lg)), "generate logits != eager"
+        g0 = gen_lg[0].cpu().numpy()[list(rows)]
+        assert_rows_close(g0, ref_step0, BF16_TOL, "generate step 0")
+        check_argmax(gen_tok[0].cpu().numpy()[list(rows)], g0, ref_step0, "generate step 0")
+        gen_only, _ = m.generate(start, ctx, steps)
+        assert torch.equal(gen_only, gen_tok)
     m.sync_status()
 
 

@@ -40,7 +40,7 @@ def test_generate_replays_from_a_graph():
     spec = small_bf16_spec()
     m, _ = build_model(spec, 31, max_batch=B, max_seq=64, max_tokens=B * S)
     toks = torch.from_numpy(syn.tokens(31, B, S, spec.vocab_size)).cuda()
-    first = m.prefill(toks).argmax(-1).to(torch.int32).contiguous()
+    _, first = m.prefill(toks, want_next=True)
     out = torch.empty((N, B), dtype=torch.int32, device="cuda")
     lg = torch.empty((N, B, spec.vocab_size), dtype=torch.float32, device="cuda")
 
@@ -104,7 +104,7 @@ def test_decode_step_replays_from_a_graph():
     spec = small_bf16_spec()
     m, _ = build_model(spec, 34, max_batch=B, max_seq=64, max_tokens=B * S)
     toks = torch.from_numpy(syn.tokens(34, B, S, spec.vocab_size)).cuda()
-    cur = m.prefill(toks).argmax(-1).to(torch.int32).contiguous()
+    _, cur = m.prefill(toks, want_next=True)
     nxt = torch.empty(B, dtype=torch.int32, device="cuda")
     lg = torch.empty((B, spec.vocab_size), dtype=torch.float32, device="cuda")
 

@@ -64,8 +64,8 @@ def test_tiny_fp32_generate_loop_matches_oracle():
     m, synth = build_model(spec, 1, max_batch=2, max_seq=40, max_tokens=40)
     toks = syn.tokens(1, 2, 17, spec.vocab_size)
     _, ls_ref, chosen_ref = O.greedy_generate(toks, 8, syn.FloatView(synth), spec)
-    l0 = m.prefill(torch.from_numpy(toks).cuda())
-    first = l0.argmax(-1).to(torch.int32).contiguous()
+    l0, first = m.prefill(torch.from_numpy(toks).cuda(), want_next=True)
+    np.testing.assert_array_equal(first.cpu().numpy(), chosen_ref[0])
     out, _ = m.generate(first, 17, 8)
     np.testing.assert_array_equal(out.cpu().numpy(), chosen_ref[1:])
     # again with logits (eager steps), after re-prefilling the cache
@@ -194,7 +194,7 @@ def test_bf16_generate_matches_eager_decode_steps():
     B, S, steps = 3, 70, 10
     m, _ = build_model(spec, 9, max_batch=B, max_seq=96, max_tokens=B * S)
     toks = torch.from_numpy(syn.tokens(9, B, S, spec.vocab_size)).cuda()
-    first = m.prefill(toks).argmax(-1).to(torch.int32).contiguous()
+    _, first = m.prefill(toks, want_next=True)
     eager = []
     cur = first
     for k in range(steps):
@@ -249,3 +249,123 @@ def test_out_of_range_token_is_reported():
         m.sync_status()
     assert e.value.status == -1
     m.sync_status()  # cleared
+
+
+# ------------------------------------------------------------------ greedy choice after prefill
+
+@pytest.mark.parametrize("all_positions", [False, True])
+def test_prefill_next_tokens_are_the_argmax_of_its_logits(all_positions):
+    say(f"small bf16 stack: prefill next_tokens (all_positions={all_positions})")
+    spec = small_bf16_spec()
+    B, S = 3, 45
+    m, synth = build_model(spec, 21, max_batch=B, max_seq=64, max_tokens=B * S)
+    toks = syn.tokens(21, B, S, spec.vocab_size)
+    lg, nxt = m.prefill(torch.from_numpy(toks).cuda(), all_positions=all_positions, want_next=True)
+    lg = lg.cpu().numpy()
+    last = lg[:, -1] if all_positions else lg
+    # lowest index among equal maxima, on the GPU's own fp32 logits: bit for bit
+    np.testing.assert_array_equal(nxt.cpu().numpy(), np.argmax(last, axis=-1))
+    ref, _ = O.prefill(toks, syn.FloatView(synth), spec)
+    check_argmax(nxt.cpu().numpy(), last, ref, "prefill next tokens")
+    m.sync_status()
+
+
+def test_first_call_inside_a_stream_capture_is_refused():
+    # the one-time set-up (rotary table, cache fill) must run eagerly: a captured first call
+    # would leave later eager calls without it
+    spec = small_bf16_spec()
+    m, _ = build_model(spec, 22, max_batch=2, max_seq=32, max_tokens=64)
+    toks = torch.from_numpy(syn.tokens(22, 2, 1, spec.vocab_size)[:, 0].copy()).cuda()
+    out = torch.empty(2, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    st = None
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        g.capture_begin()
+        try:
+            st = m.lib.llama_decode_step(m.handle, toks.data_ptr(), 2, 0, None, out.data_ptr(),
+                                         bd._stream(side))
+            msg = m.lib.llama_last_error().decode()
+        finally:
+            g.capture_end()
+    torch.cuda.synchronize()
+    assert st == -1 and "capture" in msg, (st, msg)
+    # eager use works afterwards and sets the model up
+    nxt, lg = m.decode_step(toks, 0)
+    assert np.isfinite(lg.cpu().numpy()).all()
+    m.sync_status()
+
+
+# ------------------------------------------------------------------ shapes off the common path
+
+def test_bf16_ffn_width_not_a_multiple_of_128():
+    # F = 1472 = 23 x 64: the down projection's K is not a multiple of 128, so at <= 32 rows
+    # it takes the 128 x 32 tiled GEMM on row-major input instead of the weight-streaming one
+    spec = small_bf16_spec(ffn_hidden=1472)
+    B, S, steps = 4, 40, 3
+    say(f"small bf16 stack F=1472: prefill {B} x {S}, {steps} teacher-forced decode steps")
+    m, synth = build_model(spec, 23, max_batch=B, max_seq=48, max_tokens=B * S)
+    toks = syn.tokens(23, B, S, spec.vocab_size)
+    W = syn.FloatView(synth)
+    ref0, caches = O.prefill(toks, W, spec, capacity=S + steps)
+    got0 = m.prefill(torch.from_numpy(toks).cuda()).cpu().numpy()
+    assert_rows_close(got0, ref0, BF16_TOL, "prefill logits")
+    cur = O.argmax(ref0).astype(np.int32)
+    for k in range(steps):
+        ref = O.decode_step(cur, S + k, W, spec, caches)
+        nxt, lg = m.decode_step(torch.from_numpy(cur).cuda(), S + k)
+        lg = lg.cpu().numpy()
+        assert_rows_close(lg, ref, BF16_TOL, f"decode step {k}")
+        check_argmax(nxt.cpu().numpy(), lg, ref, f"decode step {k}")
+        cur = O.argmax(ref).astype(np.int32)
+    m.sync_status()
+
+
+def test_bf16_head_dim_64_generic_attention():
+    # head_dim 64 (8 query heads over 2 KV heads at dim 512): prefill and decode attention
+    # take the generic one-wave-per-row kernel in bf16
+    spec = small_bf16_spec(n_heads=8, n_kv_heads=2, head_dim=64)
+    B, S, steps = 2, 70, 3
+    say(f"small bf16 stack d=64: prefill {B} x {S} (all positions), {steps} decode steps")
+    m, synth = build_model(spec, 24, max_batch=B, max_seq=80, max_tokens=B * S)
+    toks = syn.tokens(24, B, S, spec.vocab_size)
+    W = syn.FloatView(synth)
+    ref_all, _ = O.prefill(toks, W, spec, all_positions=True)
+    got_all = m.prefill(torch.from_numpy(toks).cuda(), all_positions=True).cpu().numpy()
+    assert_rows_close(got_all, ref_all, BF16_TOL, "prefill logits, every position")
+    ref0, caches = O.prefill(toks, W, spec, capacity=S + steps)
+    cur = O.argmax(ref0).astype(np.int32)
+    for k in range(steps):
+        ref = O.decode_step(cur, S + k, W, spec, caches)
+        nxt, lg = m.decode_step(torch.from_numpy(cur).cuda(), S + k)
+        lg = lg.cpu().numpy()
+        assert_rows_close(lg, ref, BF16_TOL, f"decode step {k}")
+        check_argmax(nxt.cpu().numpy(), lg, ref, f"decode step {k}")
+        cur = O.argmax(ref).astype(np.int32)
+    m.sync_status()
+
+
+def test_trace_records_the_residual_stream():
+    # the trace holds the embedding rows bit for bit, each layer's input, and the rows the
+    # final norm reads; llama_layer_forward on a recorded input reproduces the next one
+    spec = small_bf16_spec()
+    B, S = 2, 100
+    say(f"small bf16 stack: residual-stream trace of a {B} x {S} prefill")
+    m, synth = build_model(spec, 25, max_batch=B, max_seq=128, max_tokens=B * S)
+    toks = syn.tokens(25, B, S, spec.vocab_size)
+    tr = m.trace_hidden(B * S)
+    lg = m.prefill(torch.from_numpy(toks).cuda(), all_positions=True).cpu().numpy()
+    h = tr.cpu().numpy()
+    m.trace_hidden(None)
+    E = synth.as_float("tok_embeddings.weight", np.float32)
+    np.testing.assert_array_equal(h[0], E[toks.reshape(-1)])
+    for l in range(spec.n_layers):
+        x_in = torch.from_numpy(np.ascontiguousarray(h[l].reshape(B, S, -1))).cuda()
+        x_out = m.layer_forward(l, x_in).cpu().numpy().reshape(B * S, -1)
+        np.testing.assert_array_equal(x_out, h[l + 1], err_msg=f"layer {l}")
+    W = syn.FloatView(synth)
+    assert_rows_close(lg.reshape(B * S, -1), O.head_logits(h[spec.n_layers].astype(np.float64), W, spec),
+                      BF16_TOL, "head on the recorded final rows")
+    m.sync_status()
