@@ -159,6 +159,21 @@ llama_status llama_prefill_at(llama_model *m, const int32_t *tokens, int32_t B, 
 llama_status llama_decode_step(llama_model *m, const int32_t *tokens, int32_t B, int32_t pos,
                                float *logits, int32_t *next_tokens, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): llama_decode_step with its scratch
+ * (split-K sums of the few-row projections, decode-attention split partials, argmax
+ * partials and, when logits is NULL, the step's logits) taken from a static array of
+ * 64 MiB inside the library, one per GPU, held until the process ends, instead of the
+ * model's workspace.  The results equal llama_decode_step's bit for bit.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (two streams, or two models)
+ * race and must be serialised by the caller.  Nothing in the array needs clearing
+ * between calls.  Errors as llama_decode_step, plus CAPACITY when the step needs more than
+ * the 64 MiB (about B * (vocab * 4 + n_heads * (head_dim + 2) * 4 * ceil(max_seq / 256))
+ * bytes). */
+llama_status llama_decode_step_noalloc(llama_model *m, const int32_t *tokens, int32_t B,
+                                       int32_t pos, float *logits, int32_t *next_tokens,
+                                       hipStream_t stream);
+
 /* Decode step of a ragged batch: sequence b's token tokens[b] sits at its own position
  * positions[b] (device memory, int32 [B]); its key and value are written at that position
  * and it attends to its cache positions 0..positions[b] (so sequences of different lengths
@@ -205,7 +220,7 @@ llama_status llama_sync_status(llama_model *m, hipStream_t stream);
 
 /* Record the residual stream between the article's layers (section 预测下一个输出: the
  * embedding passes through the 32 layers in turn, then the final norm): while hidden is
- * set, each llama_prefill / llama_prefill_at / llama_decode_step(_ragged) /
+ * set, each llama_prefill / llama_prefill_at / llama_decode_step(_ragged, _noalloc) /
  * llama_generate call writes, as fp32 rows of dim values, the input of every layer l to
  * hidden[l][row] (rows = B*S in token order for prefill, B for decode; after the
  * embedding for l = 0) and the rows the final RMSNorm reads to hidden[n_layers][row] (each

@@ -48,7 +48,8 @@ class LlamaWeights(ctypes.Structure):
 
 
 EXPORTS = ["llama_kv_cache_bytes", "llama_workspace_bytes", "llama_init_weights", "llama_prefill",
-           "llama_prefill_at", "llama_decode_step", "llama_decode_step_ragged", "llama_generate", "llama_layer_forward",
+           "llama_prefill_at", "llama_decode_step", "llama_decode_step_noalloc",
+           "llama_decode_step_ragged", "llama_generate", "llama_layer_forward",
            "llama_sync_status", "llama_trace_hidden", "llama_free", "llama_last_error",
            "llama_profile_kernel", "llama_profile_read"]
 
@@ -76,6 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.llama_prefill.argtypes = [P, P, I, I, P, I, P]
     lib.llama_prefill_at.argtypes = [P, P, I, I, I, P, I, P, P]
     lib.llama_decode_step.argtypes = [P, P, I, I, P, P, P]
+    lib.llama_decode_step_noalloc.argtypes = [P, P, I, I, P, P, P]
     lib.llama_decode_step_ragged.argtypes = [P, P, I, P, P, P, P]
     lib.llama_generate.argtypes = [P, P, I, I, I, P, P, P]
     lib.llama_layer_forward.argtypes = [P, I, P, P, I, I, I, P]
@@ -88,7 +90,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.llama_last_error.argtypes = []
     lib.llama_last_error.restype = ctypes.c_char_p
     for fn in ("llama_init_weights", "llama_prefill", "llama_prefill_at", "llama_decode_step",
-               "llama_decode_step_ragged", "llama_generate",
+               "llama_decode_step_noalloc", "llama_decode_step_ragged", "llama_generate",
                "llama_layer_forward", "llama_sync_status", "llama_trace_hidden",
                "llama_profile_kernel", "llama_profile_read"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -197,6 +199,21 @@ class Model:
         check(self.lib.llama_decode_step(self.handle, _ptr(tokens), B, pos,
                                          _ptr(logits) if want_logits else None,
                                          _ptr(next_tokens), _stream(stream)))
+        return next_tokens, (logits if want_logits else None)
+
+    def decode_step_noalloc(self, tokens: torch.Tensor, pos: int, want_logits: bool = True,
+                            next_tokens=None, logits=None, stream=None):
+        """llama_decode_step_noalloc: decode_step with its scratch in the library's static
+        array (no workspace scratch)."""
+        B = tokens.shape[0]
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+        if next_tokens is None:
+            next_tokens = torch.empty(B, dtype=torch.int32, device=self.device)
+        if want_logits and logits is None:
+            logits = torch.empty((B, self.spec.vocab_size), dtype=torch.float32, device=self.device)
+        check(self.lib.llama_decode_step_noalloc(self.handle, _ptr(tokens), B, pos,
+                                                 _ptr(logits) if want_logits else None,
+                                                 _ptr(next_tokens), _stream(stream)))
         return next_tokens, (logits if want_logits else None)
 
     def trace_hidden(self, max_rows: int | None):

@@ -3,8 +3,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -92,6 +94,12 @@ llama_status validate_config(const llama_config* c) {
 }
 
 }  // namespace
+
+// Scratch of llama_decode_step_noalloc: one array per GPU, part of the library's code object,
+// held until the process ends.  Host code never uses this name as an address (on the host
+// it is only a stand-in for the symbol): the device address comes from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 struct llama_model {
     llama_config cfg;
@@ -219,7 +227,8 @@ struct Pending {
 
 // Scratch of one call: split-K sums of the few-row residual GEMMs, decode-attention split
 // partials, argmax partials and the logits of a decode step whose caller wants none.  The
-// model's workspace holds them (Scratch::of).
+// model's workspace holds them (Scratch::of); llama_decode_step_noalloc points them into the
+// library's static scratch array instead.
 struct Scratch {
     float* kpart;
     float* partials;
@@ -462,6 +471,70 @@ llama_status llama_decode_step(llama_model* m, const int32_t* tokens, int32_t B,
     if (st != LLAMA_OK) return st;
     return run_decode_step(m, tokens, B, pos, nullptr, 0, pos + 1, logits, next_tokens, nullptr,
                            nullptr, Scratch::of(m), s);
+}
+
+// Device address of the static scratch array on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+llama_status scratch_base(void** out) {
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(LLAMA_ERR_HIP, "device %d out of range", dev);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        try {
+            std::lock_guard<std::mutex> lock(g_scratch_mu);
+            p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+            if (!p) {
+                HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+                if (!p) return fail(LLAMA_ERR_HIP, "no device address for the scratch array");
+                g_scratch_ptr[dev].store(p, std::memory_order_release);
+            }
+        } catch (...) {
+            return fail(LLAMA_ERR_HIP, "scratch look-up failed");
+        }
+    }
+    *out = p;
+    return LLAMA_OK;
+}
+
+llama_status llama_decode_step_noalloc(llama_model* m, const int32_t* tokens, int32_t B,
+                                       int32_t pos, float* logits, int32_t* next_tokens,
+                                       hipStream_t s) {
+    if (!m || !tokens || !next_tokens) return fail(LLAMA_ERR_INVALID_ARG, "NULL model, tokens or next_tokens");
+    const llama_config& c = m->cfg;
+    if (B <= 0) return fail(LLAMA_ERR_SHAPE, "B must be positive (B=%d)", B);
+    if (B > c.max_batch) return fail(LLAMA_ERR_CAPACITY, "B=%d > max_batch=%d", B, c.max_batch);
+    if (pos < 0 || pos >= c.max_seq) return fail(LLAMA_ERR_CAPACITY, "pos=%d outside [0, max_seq=%d)", pos, c.max_seq);
+    if (m->trace && B > m->trace_rows)
+        return fail(LLAMA_ERR_CAPACITY, "B=%d > the trace's %d rows", B, m->trace_rows);
+    // carve the scratch this call needs; every region is written before it is read, so
+    // nothing is cleared
+    const int D = c.dim;
+    const int splits = std::max(lk::residual_splits(m->dt, B, D, c.n_heads * c.head_dim),
+                                lk::residual_splits(m->dt, B, D, c.ffn_hidden));
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+    const size_t o_kpart = take((size_t)splits * B * D * 4);
+    const size_t o_part = take(lk::decode_partials_bytes(B, c.n_heads, c.head_dim, m->seq_stride));
+    const size_t o_arg = take(lk::argmax_scratch_bytes(B, c.vocab_size));
+    const size_t o_log = logits ? off : take((size_t)B * c.vocab_size * 4);
+    if (off > kNoAllocScratchBytes)
+        return fail(LLAMA_ERR_CAPACITY, "this step needs %zu bytes of scratch; the static array "
+                    "holds %zu", off, kNoAllocScratchBytes);
+    void* base = nullptr;
+    llama_status st = scratch_base(&base);
+    if (st != LLAMA_OK) return st;
+    st = ensure_rope(m, s);
+    if (st != LLAMA_OK) return st;
+    char* sb = static_cast<char*>(base);
+    const Scratch scr{reinterpret_cast<float*>(sb + o_kpart), reinterpret_cast<float*>(sb + o_part),
+                      sb + o_arg, reinterpret_cast<float*>(sb + o_log)};
+    return run_decode_step(m, tokens, B, pos, nullptr, 0, pos + 1, logits, next_tokens, nullptr,
+                           nullptr, scr, s);
 }
 
 llama_status llama_decode_step_ragged(llama_model* m, const int32_t* tokens, int32_t B,

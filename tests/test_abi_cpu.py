@@ -137,6 +137,12 @@ def test_call_shape_and_capacity_errors_before_device_work(lib, handle):
     assert lib.llama_decode_step(handle, T, 3, 3, T, T, None) == -3
     assert "max_batch" in lib.llama_last_error().decode()
     assert lib.llama_sync_status(None, None) == -1
+    # the scratch-array decode step validates like llama_decode_step, before any device call
+    assert lib.llama_decode_step_noalloc(handle, T, 1, 32, T, T, None) == -3
+    assert lib.llama_decode_step_noalloc(handle, T, 3, 3, T, T, None) == -3
+    assert lib.llama_decode_step_noalloc(handle, T, 0, 3, T, T, None) == -2
+    assert lib.llama_decode_step_noalloc(handle, T, 1, 3, T, None, None) == -1
+    assert lib.llama_decode_step_noalloc(None, T, 1, 3, T, T, None) == -1
 
 
 def test_trace_validation_before_device_work(lib, handle):
