@@ -117,16 +117,27 @@ def measured_traffic(kind: str):
         return None
 
 
-def cpu_baseline(spec, seed: int, S: int, n_layers_sample: int):
-    """Time the CPU oracle (float32) on `n_layers_sample` of the 32 layers of the prefill
-    at S tokens plus the head; scale the per-layer time to the whole stack."""
+def cpu_baseline(spec, seed: int, S: int, n_layers_sample: int, dec_ctx: int, n_dec_layers: int = 4):
+    """Time the CPU oracle (float32) on bounded samples of the workloads:
+
+    * prefill of 1 x S tokens through `n_layers_sample` of the layers plus the head, the
+      per-layer time scaled to the whole stack (``value``, tokens/s);
+    * one decode step of one sequence at position `dec_ctx` over a cache of `dec_ctx`
+      positions (random keys and values: the time does not depend on them) through
+      `n_dec_layers` layers plus the head, scaled to the whole stack (``decode``; the oracle
+      decodes the rows of a batch one after the other, so this is its tokens/s at any batch);
+    * one layer at 17 tokens (``layer_17``).
+    ``cores`` is the number of BLAS threads the oracle's matrix products used,
+    ``affinity_cores`` the host cores this process may run on."""
+    import dataclasses
     from oracle import llama_oracle as O
     from llama_decoder_forward_amd import synthetic as syn
+    affinity = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        cores = affinity
     synth = syn.SyntheticWeights(spec, seed, cache=False)
     names = ["tok_embeddings.weight", "norm.weight", "output.weight"]
     for l in range(n_layers_sample):
@@ -145,12 +156,49 @@ def cpu_baseline(spec, seed: int, S: int, n_layers_sample: int):
     assert np.isfinite(logits).all()
     per_layer = (t2 - t1) / n_layers_sample
     est = (t1 - t0) + per_layer * spec.n_layers + (t3 - t2)
-    return {"value": S / est, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    del cache
+
+    # decode: one token at position dec_ctx over dec_ctx cached positions, through the
+    # layers already loaded
+    n_dec_layers = min(n_dec_layers, n_layers_sample)
+    dspec = dataclasses.replace(spec, n_layers=n_dec_layers)
+    dcache = O.SequenceCache(dspec, dec_ctx + 1, np.float32)
+    for l in range(n_dec_layers):
+        dcache.k[l][:, :dec_ctx] = syn.normal(seed, f"cpu.k{l}", (spec.n_kv_heads, dec_ctx, spec.head_dim))
+        dcache.v[l][:, :dec_ctx] = syn.normal(seed, f"cpu.v{l}", (spec.n_kv_heads, dec_ctx, spec.head_dim))
+    d0 = time.perf_counter()
+    xd = O.embed(toks[:1], W, np.float32)
+    d1 = time.perf_counter()
+    for l in range(n_dec_layers):
+        xd = O.layer_forward(xd, W, dspec, l, dcache, dec_ctx)
+    d2 = time.perf_counter()
+    lg = O.head_logits(xd, W, spec)
+    d3 = time.perf_counter()
+    assert np.isfinite(lg).all()
+    dec_step = (d1 - d0) + (d2 - d1) / n_dec_layers * spec.n_layers + (d3 - d2)
+    del dcache
+
+    # one layer at 17 tokens
+    x17 = syn.normal(2, "x", (17, spec.dim))
+    c17 = O.SequenceCache(dataclasses.replace(spec, n_layers=1), 17, np.float32)
+    l0 = time.perf_counter()
+    O.layer_forward(x17, W, spec, 0, c17, 0)
+    l1 = time.perf_counter()
+    return {"value": S / est, "unit": "tokens/s", "cores": int(cores),
+            "affinity_cores": int(affinity), "kind": "oracle",
             "sample": (f"prefill of 1 x {S} tokens through {n_layers_sample} of "
                        f"{spec.n_layers} layers plus the head in float32 "
                        f"({t3 - t0:.1f} s measured); per-layer time scaled to "
                        f"{spec.n_layers} layers"),
-            "seconds_measured": t3 - t0}
+            "seconds_measured": t3 - t0 + d3 - d0 + l1 - l0,
+            "decode": {"value": 1.0 / dec_step, "unit": "tokens/s",
+                       "ms_per_token": dec_step * 1e3,
+                       "sample": (f"one decode step of one sequence at position {dec_ctx} through "
+                                  f"{n_dec_layers} of {spec.n_layers} layers plus the head in "
+                                  f"float32 ({d3 - d0:.2f} s measured); per-layer time scaled; "
+                                  f"the oracle decodes the rows of a batch one after the other")},
+            "layer_17": {"ms": (l1 - l0) * 1e3,
+                         "sample": "one 8B-shaped layer at 1 x 17 tokens in float32"}}
 
 
 def long_context(spec, weights, prefill_runs: int, decode_steps: int) -> dict:
@@ -324,6 +372,31 @@ def main() -> int:
                      "avg_launch_ms": k_avg, "launches": k_n},
     }
 
+    # ---------------------------------------------------------------- one layer, 17 tokens
+    x17 = torch.from_numpy(syn.normal(2, "x", (1, 17, spec.dim))).cuda()
+    y17 = torch.empty_like(x17)
+    for _ in range(3):
+        m.layer_forward(0, x17, x_out=y17)
+    n17 = 5 if args.profile_only else 50
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(n17):
+        m.layer_forward(0, x17, x_out=y17)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    l17 = start.elapsed_time(stop) / n17
+    w_layer_bytes = 2 * (spec.dim * (spec.n_heads + 2 * spec.n_kv_heads) * spec.head_dim
+                         + spec.n_heads * spec.head_dim * spec.dim + 3 * spec.dim * spec.ffn_hidden
+                         + 2 * spec.dim)
+    result["layer_17"] = {
+        "workload": "one llama3-8b-shaped decoder layer on 1 x 17 tokens at positions 0..16 "
+                    "(llama_layer_forward)",
+        "us_per_call": l17 * 1e3, "calls": n17,
+        "hbm_gbs": w_layer_bytes / (l17 * 1e-3) / 1e9,
+        "hbm_frac": w_layer_bytes / (l17 * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    }
+    log(f"one layer at 17 tokens: {l17 * 1e3:.1f} us")
+
     # ---------------------------------------------------------------- decode
     if run_decode:
         dtoks = torch.from_numpy(syn.tokens(4, dec_B, dec_ctx, spec.vocab_size)).cuda()
@@ -443,7 +516,7 @@ def main() -> int:
         m = None
         del weights
         torch.cuda.empty_cache()
-        result["cpu_baseline"] = cpu_baseline(spec, seed, S, args.cpu_layers)
+        result["cpu_baseline"] = cpu_baseline(spec, seed, S, args.cpu_layers, dec_ctx)
     print(json.dumps(result), flush=True)
     return 0
 
