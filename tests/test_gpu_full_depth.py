@@ -205,3 +205,96 @@ def test_decode_batch32_context4096_32_layers():
         check_argmax(nxts[k][list(rows)], got, ref, f"greedy tokens, step {k}")
     say(f"  worst per-layer error {worst:.3e}")
     m.sync_status()
+
+
+def test_long_context_4x8192_32_layers():
+    """The long-context config at its full depth: 4 x 8192 tokens prefilled in one call, then
+    two greedy steps of the batch.  The residual stream of the prefill is recorded; for every
+    layer, sampled positions of sequences 0 and 3 run through the oracle's layer on the GPU's
+    own input row and the GPU's own cache of the earlier positions (a position depends on
+    nothing later), within 2e-2 of the GPU's output row, and the key and value the GPU wrote
+    there are checked too; likewise rows 0 and 3 of both decode steps, and the head."""
+    spec = syn.LLAMA3_8B
+    B, S, steps, L = 4, 8192, 2, spec.n_layers
+    seqs = (0, 3)
+    rng = np.random.default_rng(5)
+    pos = sorted(set([0, 1, 63, 64, 65, 2047, 4096, S - 2, S - 1] +
+                     [int(p) for p in rng.integers(2, S - 2, 3)]))
+    say(f"8B, {L} layers: prefill {B} x {S}, {steps} decode steps; positions {pos} of "
+        f"sequences {seqs} checked per layer")
+    m, synth = build_model(spec, 5, max_batch=B, max_seq=S + steps, max_tokens=B * S, cache=False)
+    toks = syn.tokens(5, B, S, spec.vocab_size)
+    # logits at every position, so that the final norm reads (and the trace records) the
+    # last layer's output at every sampled position
+    tr = m.trace_hidden(B * S)
+    logits, cur = m.prefill(torch.from_numpy(toks).cuda(), all_positions=True, want_next=True)
+    rows = [b * S + p for b in seqs for p in pos]
+    hid_p = tr[:, rows].cpu().numpy()                        # [L + 1, rows, D]
+    m.trace_hidden(None)
+    del tr
+    lg_p = logits[list(seqs)][:, pos].cpu().numpy().reshape(len(rows), -1)
+    last = logits[:, -1].cpu().numpy()
+    del logits
+    torch.cuda.empty_cache()
+    cur_np = cur.cpu().numpy()
+    np.testing.assert_array_equal(cur_np, np.argmax(last, axis=-1))
+    # decode: two greedy steps with the stream of the batch recorded
+    tr = m.trace_hidden(B)
+    hid_d, lgs, nxts = [], [], []
+    for k in range(steps):
+        nxt, lg = m.decode_step(cur, S + k)
+        hid_d.append(tr.cpu().numpy()[:, list(seqs)])
+        lgs.append(lg.cpu().numpy())
+        nxts.append(nxt.cpu().numpy())
+        np.testing.assert_array_equal(nxts[-1], np.argmax(lgs[-1], axis=-1))
+        cur = nxt
+    m.trace_hidden(None)
+
+    G, d = spec.n_kv_heads, spec.head_dim
+    worst = 0.0
+    for l in range(L):
+        W = _layer_weights(synth, l)
+        for i, b in enumerate(seqs):
+            kc = m.cache_k(l)[b, :, :S + steps].float().cpu().numpy()
+            vc = m.cache_v(l)[b, :, :S + steps].float().cpu().numpy()
+            # prefill rows
+            for j, p in enumerate(pos):
+                r = i * len(pos) + j
+                c = _LayerCache(l, kc[:, :p + 1].copy(), vc[:, :p + 1].copy())
+                c.k[l][:, p] = 0.0
+                c.v[l][:, p] = 0.0
+                out = O.layer_forward(hid_p[l][r:r + 1], W, spec, l, c, p)
+                err = assert_rows_close(hid_p[l + 1][r:r + 1], out, BF16_TOL,
+                                        f"layer {l}, sequence {b}, position {p}")
+                worst = max(worst, float(err.max()))
+                assert_rows_close(kc[:, p].reshape(1, -1), c.k[l][:, p].reshape(1, -1), BF16_TOL,
+                                  f"K at {p}, layer {l}, sequence {b}")
+                assert_rows_close(vc[:, p].reshape(1, -1), c.v[l][:, p].reshape(1, -1), BF16_TOL,
+                                  f"V at {p}, layer {l}, sequence {b}")
+            # decode rows
+            for k in range(steps):
+                p = S + k
+                c = _LayerCache(l, kc[:, :p + 1].copy(), vc[:, :p + 1].copy())
+                c.k[l][:, p] = 0.0
+                c.v[l][:, p] = 0.0
+                out = O.layer_forward(hid_d[k][l][i:i + 1], W, spec, l, c, p)
+                err = assert_rows_close(hid_d[k][l + 1][i:i + 1], out, BF16_TOL,
+                                        f"decode step {k}, layer {l}, sequence {b}")
+                worst = max(worst, float(err.max()))
+                assert_rows_close(kc[:, p].reshape(1, -1), c.k[l][:, p].reshape(1, -1), BF16_TOL,
+                                  f"K at {p}, layer {l}, sequence {b}")
+        del W
+        if l % 8 == 7:
+            say(f"  layers 0..{l}: worst shared-input error {worst:.3e}")
+    Wh = _head_weights(synth)
+    ref = O.head_logits(hid_p[L], Wh, spec)
+    assert_rows_close(lg_p, ref, BF16_TOL, "prefill head, sampled positions")
+    lastr = [i * len(pos) + len(pos) - 1 for i in range(len(seqs))]   # position S - 1
+    check_argmax(cur_np[list(seqs)], lg_p[lastr], ref[lastr], "prefill greedy tokens")
+    for k in range(steps):
+        ref = O.head_logits(hid_d[k][L], Wh, spec)
+        got = lgs[k][list(seqs)]
+        assert_rows_close(got, ref, BF16_TOL, f"decode head, step {k}")
+        check_argmax(nxts[k][list(seqs)], got, ref, f"decode greedy tokens, step {k}")
+    say(f"  worst per-layer error {worst:.3e}")
+    m.sync_status()
