@@ -5,6 +5,8 @@
 // blocks of 64 positions, [b][g][pos/64][d][64] (vt_offset in epilogue.hpp).
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace lk {
 
 namespace {
@@ -132,9 +134,11 @@ struct FaTile {
     bool valid;
 };
 
-__device__ __forceinline__ void fa_tile_init(FaTile& T, const bf16* __restrict__ q, int blk, int r,
-                                             int b, int g, int S, int start_pos, int H,
-                                             int group, int BQ, int lh) {
+// Rows of a workgroup's 128-row query tile: row r is query head g*group + r/BQ at position
+// blk*BQ + r%BQ of the call.  In LDS a tile row (128 d, 256 B) keeps its 16-byte chunk c
+// at slot c ^ (r & 15), as the K tile does.
+__device__ __forceinline__ void fa_tile_init(FaTile& T, int blk, int r, int g, int S,
+                                             int start_pos, int group, int BQ) {
     T.hq = g * group + r / BQ;
     T.sq = blk * BQ + r % BQ;
     T.valid = T.sq < S;
@@ -142,10 +146,6 @@ __device__ __forceinline__ void fa_tile_init(FaTile& T, const bf16* __restrict__
     T.p_lo = start_pos + blk * BQ;
     const int p_hi = start_pos + min(S, blk * BQ + BQ) - 1;
     T.nkb = (p_hi + 1 + FA_BKV - 1) / FA_BKV;   // keys this tile's block needs: 0..p_hi
-    const bf16* qrow = q + ((size_t)(b * S + (T.valid ? T.sq : 0)) * H + T.hq) * FA_D;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-        T.qf[kk] = T.valid ? *reinterpret_cast<const bf16x8*>(qrow + (kk * 2 + lh) * 8) : bf16x8{};
 #pragma unroll
     for (int i = 0; i < 4; ++i) T.o[i] = f32x16{};
     T.m = -INFINITY;
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, lr = lane & 31, lh = lane >> 5;
 
     FaTile T;
-    fa_tile_init(T, q, qb, wave * 32 + lr, b, g, S, start_pos, H, group, BQ, lh);
+    fa_tile_init(T, qb, wave * 32 + lr, g, S, start_pos, group, BQ);
     const int nkb = T.nkb;
 
     const bf16* kbase = kc + ((size_t)b * G + g) * seq_stride * FA_D;
@@ -244,38 +244,69 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     // 8 d rows) per copy; both operand reads below are conflict-free 16-byte reads.
     // Keys past the sequence's context are read too (whole 64-position blocks inside the
     // cache); the causal mask gives them probability 0 and the cache holds finite values.
+    //
+    // Addressing is kept off the vector ALU: copy i of a wave moves key rows 4 ci .. 4 ci + 3
+    // (ci = wave + 4 i) and d rows 8 ci .. 8 ci + 7, whose swizzle does not depend on i, so
+    // one per-lane byte offset serves all four copies of each tile, and the block and copy
+    // parts of the address are scalar.
+    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);   // the wave index, in a scalar
     const unsigned lds0 = lds_addr(fa_smem);
+    const unsigned koff = (unsigned)((4 * wv + (lane >> 4)) * 256 +
+                                     (((lane & 15) ^ ((4 * wv + (lane >> 4)) & 15)) * 16));
+    const unsigned voff = (unsigned)((8 * wv + (lane >> 3)) * 128 +
+                                     (((lane & 7) ^ ((4 * wv + (lane >> 4)) & 7)) * 16));
     auto issue = [&](int st, int kb) {
-        const bf16* ksrc = kbase + (size_t)kb * FA_BKV * FA_D;
-        const bf16* vsrc = vbase + (size_t)kb * FA_D * VT_BLOCK;
-        const unsigned dst = lds0 + st * FA_STAGE_BYTES;
+        const char* ksrc = reinterpret_cast<const char*>(kbase + (size_t)kb * FA_BKV * FA_D);
+        const char* vsrc = reinterpret_cast<const char*>(vbase + (size_t)kb * FA_D * VT_BLOCK);
+        const unsigned dst = lds0 + st * FA_STAGE_BYTES + wv * 1024;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ci = wave + 4 * i;
-            const int kr = 4 * ci + (lane >> 4), kcp = lane & 15;
-            lds_dma16(ksrc + kr * FA_D + ((kcp ^ (kr & 15)) * 8), dst + ci * 1024);
-        }
+        for (int i = 0; i < 4; ++i) lds_dma16_s(ksrc + i * 4096, koff, dst + i * 4096);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ci = wave + 4 * i;
-            const int vd = 8 * ci + (lane >> 3), vcp = lane & 7;
-            lds_dma16(vsrc + vd * VT_BLOCK + ((vcp ^ ((vd >> 1) & 7)) * 8), dst + FA_KBYTES + ci * 1024);
-        }
+        for (int i = 0; i < 4; ++i) lds_dma16_s(vsrc + i * 4096, voff, dst + FA_KBYTES + i * 4096);
     };
 
+    // The query tile arrives through the second stage buffer by the same direct copies (each
+    // 1 KB copy = 4 whole rows, so every global read is a full 256-byte row segment; rows
+    // past the call's tokens read its last token and are never stored), while the first
+    // key block lands in the first buffer.
     issue(0, 0);
-    for (int kb = 0; kb < nkb; ++kb) {
+    {
+        const unsigned qdst = lds0 + FA_STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int ci = wave + 4 * i;
+            const int qr = 4 * ci + (lane >> 4), slot = lane & 15;
+            const int sq = min(qb * BQ + qr % BQ, S - 1);
+            const bf16* qsrc = q + ((size_t)(b * S + sq) * H + g * group + qr / BQ) * FA_D;
+            lds_dma16(qsrc + ((slot ^ (qr & 15)) * 8), qdst + ci * 1024);
+        }
+        wait_vm_and_barrier<0>();
+        const int r = wave * 32 + lr;
+        const u32x4* qs = fa_smem + FA_STAGE_BYTES / 16;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            T.qf[kk] = __builtin_bit_cast(bf16x8, qs[r * 16 + ((kk * 2 + lh) ^ (r & 15))]);
+        // every wave's reads of the query tile end before the loop copies a key block there
+        wait_lgkm_and_barrier();
+    }
+
+    // Operand reads.  S^T = K Q^T runs on two 32-key tiles; MFMA row r of tile i is key
+    // 32i + pi(r), pi(r) = 16(r/16) + 8((r/4)%2) + 4((r/8)%2) + r%4, so that each lane's
+    // eight P values of one P.V k-step are eight consecutive keys.  K k-step kk reads chunk
+    // 2 kk + lh of its key row, at byte (32i + krow) 256 + ((2kk ^ lh ^ (krow & 15)) 16) =
+    // (ka ^ 32kk) + 8192 i; V^T k-step j of d tile td reads chunk 2j + lh of row d = 32 td
+    // + lr, at (va ^ 32j) + 4096 td.  The stage offset is a compile-time constant of each
+    // of the loop's two unrolled halves, so every read is one XOR and an immediate offset.
+    const int krow = 16 * (lr >> 4) + 8 * ((lr >> 2) & 1) + 4 * ((lr >> 3) & 1) + (lr & 3);
+    const unsigned ka = (unsigned)(krow * 256 + ((lh ^ (krow & 15)) * 16));
+    const unsigned va = (unsigned)(lr * 128 + ((lh ^ ((lr >> 1) & 7)) * 16));
+    const char* lds_c = reinterpret_cast<const char*>(fa_smem);
+    auto block = [&](int kb, auto st_c) {
+        constexpr int st = decltype(st_c)::value;
         // block kb has landed; the barrier also retires every wave's reads of the other slot
         wait_vm_and_barrier<0>();
-        if (kb + 1 < nkb) issue((kb + 1) & 1, kb + 1);
-        const u32x4* ks = fa_smem + (kb & 1) * (FA_STAGE_BYTES / 16);
-        const u32x4* vs = ks + FA_KBYTES / 16;
+        if (kb + 1 < nkb) issue(st ^ 1, kb + 1);
         const int kv0 = kb * FA_BKV;
-
-        // S^T = K Q^T: two 32-key tiles, K fragments read a quarter block ahead.  MFMA row r
-        // of tile i is key 32i + pi(r), pi(r) = 16(r/16) + 8((r/4)%2) + 4((r/8)%2) + r%4, so
-        // that each lane's eight P values of one P.V k-step are eight consecutive keys.
-        const int krow = 16 * (lr >> 4) + 8 * ((lr >> 2) & 1) + 4 * ((lr >> 3) & 1) + (lr & 3);
         f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
@@ -283,10 +314,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2) {
                 const int kk = 2 * h + k2;
-                const int ch = (kk * 2 + lh) ^ (krow & 15);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
-                    kf[k2][i] = __builtin_bit_cast(bf16x8, ks[(32 * i + krow) * 16 + ch]);
+                    kf[k2][i] = *reinterpret_cast<const bf16x8*>(
+                        lds_c + ((ka ^ (32u * kk)) + 8192 * i + st * FA_STAGE_BYTES));
             }
 #pragma unroll
             for (int k2 = 0; k2 < 2; ++k2)
@@ -300,29 +331,52 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
         // row d, the 16-byte chunk 2j + lh
 #pragma unroll
         for (int td = 0; td < 4; ++td) {
-            const int d = 32 * td + lr;
             bf16x8 vf[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                vf[j] = __builtin_bit_cast(bf16x8, vs[d * 8 + ((2 * j + lh) ^ ((d >> 1) & 7))]);
+                vf[j] = *reinterpret_cast<const bf16x8*>(
+                    lds_c + ((va ^ (32u * j)) + 4096 * td + FA_KBYTES + st * FA_STAGE_BYTES));
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 T.o[td] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pf[j], T.o[td], 0, 0, 0);
         }
+    };
+    int kb = 0;
+    for (; kb + 1 < nkb; kb += 2) {
+        block(kb, std::integral_constant<int, 0>{});
+        block(kb + 1, std::integral_constant<int, 1>{});
     }
+    if (kb < nkb) block(kb, std::integral_constant<int, 0>{});
 
-    if (!T.valid) return;
-    const float inv = 1.0f / T.l;
+    // The normalised output goes through LDS (the first stage buffer, free once every wave
+    // is past its last key block) and leaves as whole 16-byte chunks of each row: lane
+    // (lr, lh) holds d = 32 td + 8 gg + 4 lh .. +3 of its row, half of chunk 4 td + gg.
+    wait_lgkm_and_barrier();
+    {
+        const float inv = 1.0f / T.l;
+        const int r = wave * 32 + lr;
+        char* ob = reinterpret_cast<char*>(fa_smem);
 #pragma unroll
-    for (int td = 0; td < 4; ++td)
+        for (int td = 0; td < 4; ++td)
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) {
-            float v[4] = {T.o[td][4 * gg] * inv, T.o[td][4 * gg + 1] * inv,
-                          T.o[td][4 * gg + 2] * inv, T.o[td][4 * gg + 3] * inv};
-            store4(out + act_offset(b * S + T.sq, T.hq * FA_D + 32 * td + 8 * gg + 4 * lh,
-                                    H * FA_D, out_pack),
-                   v);
+            for (int gg = 0; gg < 4; ++gg) {
+                const int c = 4 * td + gg;
+                *reinterpret_cast<bf16x4*>(ob + r * 256 + ((c ^ (r & 15)) * 16) + lh * 8) =
+                    bf16x4{from_f32<bf16>(T.o[td][4 * gg] * inv), from_f32<bf16>(T.o[td][4 * gg + 1] * inv),
+                           from_f32<bf16>(T.o[td][4 * gg + 2] * inv), from_f32<bf16>(T.o[td][4 * gg + 3] * inv)};
+            }
+    }
+    wait_lgkm_and_barrier();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int ch = i * 256 + t, r = ch >> 4, c = ch & 15;
+        const int sq = qb * BQ + r % BQ;
+        if (sq < S) {
+            const u32x4 v = fa_smem[r * 16 + (c ^ (r & 15))];
+            *reinterpret_cast<u32x4*>(out + act_offset(b * S + sq, (g * group + r / BQ) * FA_D + c * 8,
+                                                       H * FA_D, out_pack)) = v;
         }
+    }
 }
 
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {

@@ -65,6 +65,15 @@ __device__ __forceinline__ void lds_dma16(const void* gptr, unsigned lds_byte) {
                  : "memory");
 }
 
+// The same copy addressed as a 64-bit base in scalar registers plus a 32-bit byte offset
+// per lane (the base and the LDS address must be uniform across the wave).
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, unsigned voff, unsigned lds_byte) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds_byte), "v"(voff), "s"(sbase)
+                 : "memory");
+}
+
 // Wait until at most N of this wave's vector-memory operations are outstanding, then
 // synchronise the workgroup.
 template <int N>
