@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
             const bf16* qsrc = q + ((size_t)(b * S + sq) * H + g * group + qr / BQ) * FA_D;
             lds_dma16(qsrc + ((slot ^ (qr & 15)) * 8), qdst + ci * 1024);
         }
-        wait_vm_and_barrier<0>();
+        wait_copies_and_barrier();
         const int r = wave * 32 + lr;
         const u32x4* qs = fa_smem + FA_STAGE_BYTES / 16;
 #pragma unroll
@@ -303,8 +303,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     const char* lds_c = reinterpret_cast<const char*>(fa_smem);
     auto block = [&](int kb, auto st_c) {
         constexpr int st = decltype(st_c)::value;
-        // block kb has landed; the barrier also retires every wave's reads of the other slot
-        wait_vm_and_barrier<0>();
+        // block kb has landed, and every wave's reads of the other slot have returned
+        wait_copies_and_barrier();
         if (kb + 1 < nkb) issue(st ^ 1, kb + 1);
         const int kv0 = kb * FA_BKV;
         f32x16 sacc[2] = {f32x16{}, f32x16{}};

@@ -74,11 +74,13 @@ __device__ __forceinline__ void lds_dma16_s(const void* sbase, unsigned voff, un
                  : "memory");
 }
 
-// Wait until at most N of this wave's vector-memory operations are outstanding, then
-// synchronise the workgroup.
-template <int N>
-__device__ __forceinline__ void wait_vm_and_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+// Wait until this wave's copies into LDS have landed and its own LDS reads have returned,
+// then synchronise the workgroup: after it every wave's copies are visible and no wave still
+// reads a buffer that a copy issued next may overwrite.  (A read's data being consumed later
+// in program order is no guarantee: the compiler may move the consuming instructions past the
+// barrier.)
+__device__ __forceinline__ void wait_copies_and_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
 // Wait for this wave's LDS operations, then synchronise the workgroup (outstanding global

@@ -297,3 +297,26 @@ def test_chunked_prefill_8b_widths():
     say("  oracle (float32), row 0")
     ref, _ = O.prefill(toks[:1], W, spec, all_positions=True, dtype=np.float32)
     assert_rows_close(got, ref[0, 1024:], BF16_TOL, "chunk 2 logits")
+
+
+def test_chunked_prefill_8b_widths_repeatable():
+    """The same two-chunk prefill, repeated three times on one model: logits and cache are
+    identical bit for bit each time (every kernel's result depends only on its inputs; a
+    workgroup that read an LDS buffer while another wave's next copy was landing in it would
+    show up here as a run-to-run difference)."""
+    say("8B widths, 2 layers, chunked prefill repeated 3 times: bitwise repeatable")
+    spec = _spec(2)
+    m, _ = build_model(spec, 17, max_batch=2, max_seq=2048, max_tokens=2048, cache=False)
+    toks = syn.tokens(17, 2, 2048, spec.vocab_size)
+    first = None
+    for rep in range(3):
+        m.prefill(torch.from_numpy(np.ascontiguousarray(toks[:, :1024])).cuda())
+        got = m.prefill(torch.from_numpy(np.ascontiguousarray(toks[:, 1024:])).cuda(),
+                        all_positions=True, start_pos=1024)
+        state = (got, m.cache_k(1).clone(), m.cache_v(1).clone())
+        if first is None:
+            first = state
+        else:
+            for a, b, what in zip(first, state, ("logits", "layer-1 K cache", "layer-1 V cache")):
+                assert torch.equal(a, b), f"repeat {rep}: {what} differs from the first run"
+    m.sync_status()
