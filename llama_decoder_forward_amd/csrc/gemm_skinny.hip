@@ -23,23 +23,27 @@ namespace {
 constexpr int SK_ROWS = 16;  // weight rows per strip
 constexpr int SK_KB = 128;   // k per block
 
+// Workgroup x owns weight rows n0 = x * rows .. min(N, n0 + rows) - 1 (rows a multiple of 8,
+// at most 16 RT); the lanes of rows past the end load the last row again (the same lines as
+// that row's lanes, so no extra memory traffic) and their results are dropped.
 template <int NW, int RT, int MB, bool DUAL, int BUDGET, typename Epi>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
     const bf16* __restrict__ A, int pack, WeightRows<bf16> W, WeightRows<bf16> W3, int M, int N,
-    int K, Epi epi) {
+    int K, int rows, Epi epi) {
     constexpr int NA = DUAL ? 2 : 1;
     __shared__ f32x4 red[NW > 1 ? NW - 1 : 1][NA * RT * MB][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int strip = blockIdx.x;             // RT tiles of 16 weight rows
-    const int n0 = strip * SK_ROWS * RT;
+    const int n0 = blockIdx.x * rows;
+    const int n_end = min(N, n0 + rows);
     const int col = lane & 15, kq = lane >> 4;
 
     const bf16* wrow[RT];
     const bf16* w3row[DUAL ? RT : 1];
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-        wrow[r] = W.row(n0 + 16 * r + col) + kq * 8;
-        if constexpr (DUAL) w3row[r] = W3.row(n0 + 16 * r + col) + kq * 8;
+        const int n = min(n0 + 16 * r + col, n_end - 1);
+        wrow[r] = W.row(n) + kq * 8;
+        if constexpr (DUAL) w3row[r] = W3.row(n) + kq * 8;
     }
     // packed activations (act_offset): run (kb, j, mb) is 32 R values; lane (col, kq) takes
     // the 8 of row col % R
@@ -149,7 +153,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int m = mb * 16 + col;
-            if (m >= M) continue;
+            if (m >= M || n0 + 16 * r + 4 * kq >= n_end) continue;
             float v[4] = {acc[r][mb][0], acc[r][mb][1], acc[r][mb][2], acc[r][mb][3]};
             if constexpr (DUAL) {
                 float u[4] = {acc3[r][mb][0], acc3[r][mb][1], acc3[r][mb][2], acc3[r][mb][3]};
@@ -170,12 +174,13 @@ hipError_t launch_mb(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     const int strips = g.N / (SK_ROWS * RT);
     const bf16* A = (const bf16*)g.A;
     // waves per strip: enough waves in flight to cover HBM latency (about 2-4k waves)
+    const int rows = SK_ROWS * RT;
     if (strips >= 2048)
-        gemm_skinny_kernel<2, RT, MB, DUAL, 96, Epi><<<strips, 128, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
+        gemm_skinny_kernel<2, RT, MB, DUAL, 96, Epi><<<strips, 128, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, rows, e);
     else if (strips >= 384)
-        gemm_skinny_kernel<4, RT, MB, DUAL, 96, Epi><<<strips, 256, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
+        gemm_skinny_kernel<4, RT, MB, DUAL, 96, Epi><<<strips, 256, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, rows, e);
     else
-        gemm_skinny_kernel<8, RT, MB, DUAL, 96, Epi><<<strips, 512, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, e);
+        gemm_skinny_kernel<8, RT, MB, DUAL, 96, Epi><<<strips, 512, 0, s>>>(A, g.a_pack, W, W3, g.M, g.N, g.K, rows, e);
     return hipGetLastError();
 }
 
@@ -202,7 +207,7 @@ hipError_t launch_split(const GemmArgs<void>& g, float* part, int splits, hipStr
     const dim3 grid(g.N / (SK_ROWS * SPLIT_RT), splits);
     gemm_skinny_kernel<LLAMA_SPLIT_NW, SPLIT_RT, MB, false, LLAMA_SPLIT_BUDGET, EpiPartial>
         <<<grid, LLAMA_SPLIT_NW * 64, 0, s>>>((const bf16*)g.A, g.a_pack, bf16_rows(g.W),
-                                              bf16_rows(g.W3), g.M, g.N, g.K, e);
+                                              bf16_rows(g.W3), g.M, g.N, g.K, SK_ROWS * SPLIT_RT, e);
     return hipGetLastError();
 }
 
@@ -253,6 +258,35 @@ hipError_t gemm_residual_split(Dt dt, const GemmArgs<void>& g, float* part, int 
 //   - Q/K/V: at batch 4 RT 2 is slower (17 -> 21 us), so RT 1; from 17 rows on (two or
 //     more 16-row blocks) two activation bytes per weight byte make RT 2 pay (batch 32:
 //     24.6 -> 21.7 us).
+// Compute units of the current device (the balanced launches give each one workgroup).
+int cu_count() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            return 256;
+    }
+    return n;
+}
+
+#ifndef LLAMA_SK_BALANCE
+#define LLAMA_SK_BALANCE 1
+#endif
+
+// Weight rows per workgroup when whole strips of 16 RT rows would leave compute units idle
+// (fewer strips than units): an equal share of N per unit, rounded up to 8 rows, or 0 when
+// the strips fill the device or the share exceeds 16 RT rows.
+int balanced_rows(int N, int RT) {
+    if (!LLAMA_SK_BALANCE) return 0;
+    const int cus = cu_count();
+    if (N / (SK_ROWS * RT) >= cus) return 0;
+    const int rows = ((N + cus - 1) / cus + 7) / 8 * 8;
+    return rows <= SK_ROWS * RT && rows > SK_ROWS * (RT / 2) ? rows : 0;
+}
+
 template <bool DUAL, typename Epi>
 hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     if (g.a_pack != act_pack(Dt::BF16, g.M, g.N, g.K)) return hipErrorInvalidValue;
@@ -260,9 +294,10 @@ hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
     const bool wide = g.N >= 16384;
     if constexpr (DUAL) {
         if (mb == 2 && g.N % (SK_ROWS * 4) == 0) {
-            const int strips = g.N / (SK_ROWS * 4);
-            gemm_skinny_kernel<4, 4, 2, DUAL, 96, Epi><<<strips, 256, 0, s>>>(
-                (const bf16*)g.A, g.a_pack, bf16_rows(g.W), bf16_rows(g.W3), g.M, g.N, g.K, e);
+            const int bal = balanced_rows(g.N, 4);
+            const int rows = bal > 0 ? bal : SK_ROWS * 4;
+            gemm_skinny_kernel<4, 4, 2, DUAL, 96, Epi><<<(g.N + rows - 1) / rows, 256, 0, s>>>(
+                (const bf16*)g.A, g.a_pack, bf16_rows(g.W), bf16_rows(g.W3), g.M, g.N, g.K, rows, e);
             return hipGetLastError();
         }
         if (mb <= 2 && g.N % (SK_ROWS * 2) == 0) {
@@ -277,7 +312,15 @@ hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
         if (mb == 1) return launch_mb<1, 1, DUAL>(g, e, s);
         if (mb == 2 && wide && g.N % (SK_ROWS * 8) == 0) return launch_mb<8, 2, DUAL>(g, e, s);
         if (mb == 2 && wide && g.N % (SK_ROWS * 4) == 0) return launch_mb<4, 2, DUAL>(g, e, s);
-        if (mb == 2 && g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 2, DUAL>(g, e, s);
+        if (mb == 2 && g.N % (SK_ROWS * 2) == 0) {
+            const int bal = balanced_rows(g.N, 2);
+            if (bal > 0) {
+                gemm_skinny_kernel<8, 2, 2, DUAL, 96, Epi><<<(g.N + bal - 1) / bal, 512, 0, s>>>(
+                    (const bf16*)g.A, g.a_pack, bf16_rows(g.W), bf16_rows(g.W3), g.M, g.N, g.K, bal, e);
+                return hipGetLastError();
+            }
+            return launch_mb<2, 2, DUAL>(g, e, s);
+        }
         if (mb == 2) return launch_mb<1, 2, DUAL>(g, e, s);
         if (g.N % (SK_ROWS * 2) == 0) return launch_mb<2, 4, DUAL>(g, e, s);
         return launch_mb<1, 4, DUAL>(g, e, s);
