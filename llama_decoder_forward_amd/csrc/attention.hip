@@ -383,14 +383,12 @@ hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
     const int group = a.H / a.G, BQ = FA_ROWS / group;
     const int nqb = (a.S + BQ - 1) / BQ;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_D);
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_mfma_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(2 * FA_STAGE_BYTES));
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static PerDevice attr;
+    hipError_t e = attr.once([](int) {
+        return hipFuncSetAttribute((const void*)attn_prefill_mfma_kernel,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * FA_STAGE_BYTES));
+    });
+    if (e != hipSuccess) return e;
     attn_prefill_mfma_kernel<<<nqb * a.G * a.B, 256, 2 * FA_STAGE_BYTES, s>>>(
         (const bf16*)a.q, (const bf16*)a.kc, (const bf16*)a.vc, (bf16*)a.out, a.S, a.start_pos,
         a.H, a.G, a.seq_stride, scale_log2, nqb, a.out_pack);

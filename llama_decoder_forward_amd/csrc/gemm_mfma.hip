@@ -249,12 +249,11 @@ hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s, int 
     constexpr size_t lds_bytes = (size_t)2 * ROWS * BK * 2;
     static_assert(lds_bytes <= 160 * 1024, "LDS");
     auto kern = gemm_mfma_kernel<BN, BM, BK, WN, WM, DUAL, Epi>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
-        if (err != hipSuccess) return err;
-        attr_set = true;
-    }
+    static PerDevice attr;
+    hipError_t err = attr.once([&](int) {
+        return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
+    });
+    if (err != hipSuccess) return err;
     const int tiles = ((g.N - n_begin + BN - 1) / BN) * ((g.M + BM - 1) / BM);
     kern<<<tiles, WN * WM * 64, lds_bytes, s>>>((const bf16*)g.A, g.lda, W, W3, g.M, g.N, g.K,
                                                 n_begin, e);

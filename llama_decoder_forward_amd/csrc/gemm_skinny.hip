@@ -258,16 +258,22 @@ hipError_t gemm_residual_split(Dt dt, const GemmArgs<void>& g, float* part, int 
 //   - Q/K/V: at batch 4 RT 2 is slower (17 -> 21 us), so RT 1; from 17 rows on (two or
 //     more 16-row blocks) two activation bytes per weight byte make RT 2 pay (batch 32:
 //     24.6 -> 21.7 us).
-// Compute units of the current device (the balanced launches give each one workgroup).
+// Compute units of the current device (the balanced launches give each one workgroup);
+// 256 if the device cannot be queried.
 int cu_count() {
-    static int n = 0;
-    if (n == 0) {
-        int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            n = v;
-        else
-            return 256;
+    static PerDevice known;
+    static std::atomic<int> cus[64];
+    int n = 256;
+    const hipError_t e = known.once([](int dev) {
+        int v = 0;
+        hipError_t r = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (r == hipSuccess && v > 0 && dev < 64) cus[dev].store(v, std::memory_order_relaxed);
+        return r;
+    });
+    int dev = 0;
+    if (e == hipSuccess && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64) {
+        const int v = cus[dev].load(std::memory_order_relaxed);
+        if (v > 0) n = v;
     }
     return n;
 }

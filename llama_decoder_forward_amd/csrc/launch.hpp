@@ -3,9 +3,29 @@
 #pragma once
 #include "epilogue.hpp"
 
+#include <atomic>
+
 namespace lk {
 
 enum class Dt { BF16, F32 };
+
+// Per-device, set-once state of the launchers (kernel attributes, device properties): a bit
+// per device ordinal below 64, safe to test and set from several host threads.
+struct PerDevice {
+    std::atomic<unsigned long long> done{0};
+    // Run `set` once on the current device; later calls on that device return at once.
+    template <typename F>
+    hipError_t once(F&& set) {
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        const unsigned long long bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+        if (bit != 0 && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+        e = set(dev);
+        if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+        return e;
+    }
+};
 
 // ---- elementwise / reductions (elementwise.hip)
 hipError_t rope_table(float2* rope, int max_seq, int d, float theta, hipStream_t s);
