@@ -158,25 +158,30 @@ def cpu_baseline(spec, seed: int, S: int, n_layers_sample: int, dec_ctx: int, n_
     est = (t1 - t0) + per_layer * spec.n_layers + (t3 - t2)
     del cache
 
-    # decode: one token at position dec_ctx over dec_ctx cached positions, through the
-    # layers already loaded
+    # decode: one token at position ctx over ctx cached positions, through the layers
+    # already loaded, scaled to the whole stack
     n_dec_layers = min(n_dec_layers, n_layers_sample)
     dspec = dataclasses.replace(spec, n_layers=n_dec_layers)
-    dcache = O.SequenceCache(dspec, dec_ctx + 1, np.float32)
-    for l in range(n_dec_layers):
-        dcache.k[l][:, :dec_ctx] = syn.normal(seed, f"cpu.k{l}", (spec.n_kv_heads, dec_ctx, spec.head_dim))
-        dcache.v[l][:, :dec_ctx] = syn.normal(seed, f"cpu.v{l}", (spec.n_kv_heads, dec_ctx, spec.head_dim))
-    d0 = time.perf_counter()
-    xd = O.embed(toks[:1], W, np.float32)
-    d1 = time.perf_counter()
-    for l in range(n_dec_layers):
-        xd = O.layer_forward(xd, W, dspec, l, dcache, dec_ctx)
-    d2 = time.perf_counter()
-    lg = O.head_logits(xd, W, spec)
-    d3 = time.perf_counter()
-    assert np.isfinite(lg).all()
-    dec_step = (d1 - d0) + (d2 - d1) / n_dec_layers * spec.n_layers + (d3 - d2)
-    del dcache
+
+    def decode_step_time(ctx):
+        dcache = O.SequenceCache(dspec, ctx + 1, np.float32)
+        for l in range(n_dec_layers):
+            dcache.k[l][:, :ctx] = syn.normal(seed, f"cpu.k{l}", (spec.n_kv_heads, ctx, spec.head_dim))
+            dcache.v[l][:, :ctx] = syn.normal(seed, f"cpu.v{l}", (spec.n_kv_heads, ctx, spec.head_dim))
+        d0 = time.perf_counter()
+        xd = O.embed(toks[:1], W, np.float32)
+        d1 = time.perf_counter()
+        for l in range(n_dec_layers):
+            xd = O.layer_forward(xd, W, dspec, l, dcache, ctx)
+        d2 = time.perf_counter()
+        lg = O.head_logits(xd, W, spec)
+        d3 = time.perf_counter()
+        assert np.isfinite(lg).all()
+        return (d1 - d0) + (d2 - d1) / n_dec_layers * spec.n_layers + (d3 - d2), d3 - d0
+
+    dec_step, d_meas = decode_step_time(dec_ctx)
+    long_ctx = 8192
+    dec_long, dl_meas = decode_step_time(long_ctx)
 
     # one layer at 17 tokens
     x17 = syn.normal(2, "x", (17, spec.dim))
@@ -190,13 +195,17 @@ def cpu_baseline(spec, seed: int, S: int, n_layers_sample: int, dec_ctx: int, n_
                        f"{spec.n_layers} layers plus the head in float32 "
                        f"({t3 - t0:.1f} s measured); per-layer time scaled to "
                        f"{spec.n_layers} layers"),
-            "seconds_measured": t3 - t0 + d3 - d0 + l1 - l0,
+            "seconds_measured": t3 - t0 + d_meas + dl_meas + l1 - l0,
             "decode": {"value": 1.0 / dec_step, "unit": "tokens/s",
                        "ms_per_token": dec_step * 1e3,
                        "sample": (f"one decode step of one sequence at position {dec_ctx} through "
                                   f"{n_dec_layers} of {spec.n_layers} layers plus the head in "
-                                  f"float32 ({d3 - d0:.2f} s measured); per-layer time scaled; "
+                                  f"float32 ({d_meas:.2f} s measured); per-layer time scaled; "
                                   f"the oracle decodes the rows of a batch one after the other")},
+            "decode_long_context": {"value": 1.0 / dec_long, "unit": "tokens/s",
+                                    "ms_per_token": dec_long * 1e3,
+                                    "sample": (f"the same at position {long_ctx} "
+                                               f"({dl_meas:.2f} s measured)")},
             "layer_17": {"ms": (l1 - l0) * 1e3,
                          "sample": "one 8B-shaped layer at 1 x 17 tokens in float32"}}
 
