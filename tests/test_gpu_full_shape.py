@@ -320,3 +320,30 @@ def test_chunked_prefill_8b_widths_repeatable():
             for a, b, what in zip(first, state, ("logits", "layer-1 K cache", "layer-1 V cache")):
                 assert torch.equal(a, b), f"repeat {rep}: {what} differs from the first run"
     m.sync_status()
+
+
+def test_mha_8b_widths():
+    """Multi-head attention (32 KV heads, one per query head) at the 8B widths, 1 layer:
+    prefill of 2 x 300 tokens at every position (128-position query blocks, two key blocks
+    across the diagonal, a ragged last block) and two teacher-forced decode steps, against
+    the oracle on both rows."""
+    say("8B widths, MHA (32/32), 1 layer: prefill 2 x 300 at every position, 2 decode steps")
+    spec = dataclasses.replace(syn.LLAMA3_8B, n_layers=1, n_kv_heads=32)
+    B, S, steps = 2, 300, 2
+    m, synth = build_model(spec, 21, max_batch=B, max_seq=S + steps, max_tokens=B * S, cache=False)
+    toks = syn.tokens(21, B, S, spec.vocab_size)
+    got = m.prefill(torch.from_numpy(toks).cuda(), all_positions=True).cpu().numpy()
+    W = _oracle_weights(synth, 1)
+    say("  oracle (float32)")
+    ref, caches = O.prefill(toks, W, spec, capacity=S + steps, all_positions=True, dtype=np.float32)
+    for b in range(B):
+        assert_rows_close(got[b], ref[b], BF16_TOL, f"prefill logits, sequence {b}")
+    cur_ref = O.argmax(ref[:, -1]).astype(np.int32)
+    for k in range(steps):
+        nxt, lg = m.decode_step(torch.from_numpy(cur_ref).cuda(), S + k)
+        lg = lg.cpu().numpy()
+        r = O.decode_step(cur_ref, S + k, W, spec, caches, dtype=np.float32)
+        assert_rows_close(lg, r, BF16_TOL, f"decode step {k}")
+        check_argmax(nxt.cpu().numpy(), lg, r, f"decode step {k}")
+        cur_ref = O.argmax(r).astype(np.int32)
+    m.sync_status()
