@@ -43,7 +43,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 template <int BN, int BM, int BK, int WN, int WM, bool DUAL, typename Epi>
 __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
     const bf16* __restrict__ A, int lda, WeightRows<bf16> W, WeightRows<bf16> W3, int M, int N,
-    int K, int n_begin, Epi epi) {
+    int K, int n_begin, int group_m, Epi epi) {
     constexpr int NW = WN * WM;
     constexpr int NA = DUAL ? 2 : 1;
     constexpr int ROWS = NA * BN + BM;
@@ -67,14 +67,13 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
     const int tiles = nt_m * nt_n;
     int bid = blockIdx.x;
     // workgroups are dealt round-robin to the 8 XCDs: give each XCD a contiguous run of
-    // tiles, ordered in groups of up to GROUP_M token tiles x all weight strips (token
-    // tiles fastest), so that the ~32 tiles an XCD runs at once cover about 8 token tiles
-    // x 4 weight strips and share their panels in that XCD's L2
+    // tiles, ordered in bands of up to group_m token tiles x all weight strips (token tiles
+    // fastest), so that the ~32 tiles an XCD runs at once cover group_m token tiles x
+    // 32 / group_m weight strips and share their panels in that XCD's L2
     if (tiles % 8 == 0) bid = (bid & 7) * (tiles >> 3) + (bid >> 3);
-    constexpr int GROUP_M = 8;
-    const int per_group = GROUP_M * nt_n;
-    const int first_m = (bid / per_group) * GROUP_M;
-    const int gsize = min(nt_m - first_m, GROUP_M);
+    const int per_group = group_m * nt_n;
+    const int first_m = (bid / per_group) * group_m;
+    const int gsize = min(nt_m - first_m, group_m);
     const int tile_m = first_m + (bid % per_group) % gsize, tile_n = (bid % per_group) / gsize;
     const int n0 = n_begin + tile_n * BN, m0 = tile_m * BM;
 
@@ -254,9 +253,18 @@ hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s, int 
         return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes);
     });
     if (err != hipSuccess) return err;
-    const int tiles = ((g.N - n_begin + BN - 1) / BN) * ((g.M + BM - 1) / BM);
+    const int nt_m = (g.M + BM - 1) / BM;
+    const int tiles = ((g.N - n_begin + BN - 1) / BN) * nt_m;
+    // Token tiles per band of the tile order, measured on MI355X (8B-shaped layer): the
+    // SwiGLU pair runs fastest with bands of 2 token tiles at 2048 tokens (446 -> 430 us
+    // against 8) and of 4 beyond (8192 tokens 1656 -> 1562 us, 32768 tokens 6702 -> 6407
+    // us); the other GEMMs with bands of 8, except a long K at many token tiles (W2 at
+    // 32768 tokens 3145 -> 3078 us with 2).
+    int group_m = 8;
+    if (DUAL) group_m = nt_m <= 8 ? 2 : 4;
+    else if (g.K >= 8192 && nt_m > 8) group_m = 2;
     kern<<<tiles, WN * WM * 64, lds_bytes, s>>>((const bf16*)g.A, g.lda, W, W3, g.M, g.N, g.K,
-                                                n_begin, e);
+                                                n_begin, group_m, e);
     return hipGetLastError();
 }
 
