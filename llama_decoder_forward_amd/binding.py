@@ -283,26 +283,48 @@ class Model:
     def _elem(self):
         return torch.bfloat16 if self.spec.dtype == "bf16" else torch.float32
 
+    def kv_packed(self) -> bool:
+        """Whether the library keeps this model's KV cache in its packed layout: bf16 with
+        head_dim 128 and at most 16 query heads per KV head dividing 128, i.e. exactly the
+        shapes whose attention runs on the matrix-core kernels."""
+        c = self.cfg
+        group = c.n_heads // c.n_kv_heads
+        return (self.spec.dtype == "bf16" and c.head_dim == 128 and group <= 16
+                and 128 % group == 0)
+
     def cache_k(self, layer: int) -> torch.Tensor:
-        """K cache of one layer as [max_batch, G, seq_stride, d]."""
+        """K cache of one layer as [max_batch, G, seq_stride, d] (a view of the plain layout,
+        or a reordered copy of the packed one)."""
         c = self.cfg
         n = c.max_batch * c.n_kv_heads * self.seq_stride * c.head_dim
         es = 2 if self.spec.dtype == "bf16" else 4
         base = layer * 2 * n * es
-        return self.kv[base:base + n * es].view(self._elem()).view(
+        raw = self.kv[base:base + n * es].view(self._elem())
+        if not self.kv_packed():
+            return raw.view(c.max_batch, c.n_kv_heads, self.seq_stride, c.head_dim)
+        # packed: within a 64-position block, [t/2][t%2][jj][kq][col/4][col%4][e] holds key
+        # r = 32 (t/2) + 8 (col/4) + 4 (t%2) + col%4, dimension 32 jj + 8 kq + e
+        blk = raw.view(c.max_batch, c.n_kv_heads, self.seq_stride // 64, 2, 2, 4, 4, 4, 4, 8)
+        return blk.permute(0, 1, 2, 3, 7, 4, 8, 5, 6, 9).reshape(
             c.max_batch, c.n_kv_heads, self.seq_stride, c.head_dim)
 
     def cache_v(self, layer: int) -> torch.Tensor:
-        """V cache of one layer as [max_batch, G, seq_stride, d] (a view of the stored
-        layout, which is transposed within blocks of 64 positions: [b][g][pos/64][d][64])."""
+        """V cache of one layer as [max_batch, G, seq_stride, d] (from the stored layout:
+        transposed within blocks of 64 positions, [b][g][pos/64][d][64], or packed)."""
         c = self.cfg
         n = c.max_batch * c.n_kv_heads * self.seq_stride * c.head_dim
         es = 2 if self.spec.dtype == "bf16" else 4
         base = (layer * 2 + 1) * n * es
-        vt = self.kv[base:base + n * es].view(self._elem()).view(
-            c.max_batch, c.n_kv_heads, self.seq_stride // 64, c.head_dim, 64)
-        return vt.permute(0, 1, 2, 4, 3).reshape(c.max_batch, c.n_kv_heads, self.seq_stride,
-                                                 c.head_dim)
+        raw = self.kv[base:base + n * es].view(self._elem())
+        if not self.kv_packed():
+            vt = raw.view(c.max_batch, c.n_kv_heads, self.seq_stride // 64, c.head_dim, 64)
+            return vt.permute(0, 1, 2, 4, 3).reshape(c.max_batch, c.n_kv_heads,
+                                                     self.seq_stride, c.head_dim)
+        # packed: within a 64-position block, [dt][j][kq][col][e] holds dimension 16 dt + col
+        # of key r = 32 j + 8 kq + e
+        blk = raw.view(c.max_batch, c.n_kv_heads, self.seq_stride // 64, 8, 2, 4, 16, 8)
+        return blk.permute(0, 1, 2, 4, 5, 7, 3, 6).reshape(
+            c.max_batch, c.n_kv_heads, self.seq_stride, c.head_dim)
 
     def free(self):
         if getattr(self, "handle", None):

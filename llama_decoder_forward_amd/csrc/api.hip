@@ -269,7 +269,8 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
     lk::GemmArgs<void> qkv = gemm_args(m, m->h(), D, w.wq, T, Nq + 2 * Nk, D);
     qkv.W = WeightRows<void>{w.wq, w.wk, w.wv, Nq, Nq + Nk, D};
     EpiQKV<void> eq{m->q(), m->kc(l), m->vc(l), m->rope(), Nq, Nk, d, S, start_pos, G,
-                    m->seq_stride, pos_dev, pos_stride, c.max_seq};
+                    m->seq_stride, pos_dev, pos_stride, c.max_seq,
+                    lk::kv_cache_packed(m->dt, H, G, d) ? 1 : 0};
     {
         ProfScope ps(m, LLAMA_KERNEL_QKV, s);
         HIP_TRY(lk::gemm_qkv(m->dt, qkv, eq, s));

@@ -15,6 +15,33 @@ __host__ __device__ __forceinline__ size_t vt_offset(size_t ctx_index, int pos, 
            (pos % VT_BLOCK);
 }
 
+// Packed KV-cache layout of the bf16 matrix-core attention path (head_dim 128).  A block of
+// 64 positions of one (sequence, KV head) context keeps the same 8192-element place as in the
+// plain layouts, but is ordered as the decode attention loads it: sixteen runs of 1 KB, each
+// the operand of one 16-byte-per-lane load, so that every load is one contiguous 1 KB run.
+//  - K: run t * 4 + jj holds, at lane l = col + 16 kq, the 8 values d = 32 jj + 8 kq .. of
+//    key r = 32 (t / 2) + 8 (col / 4) + 4 (t % 2) + col % 4 of the block;
+//  - V: run dt * 2 + j holds, at lane l = col + 16 kq, the values of dimension d = 16 dt + col
+//    for keys r = 32 j + 8 kq .. +7 of the block.
+// The prefill attention's direct global -> LDS copies address the same 16-byte pieces, so its
+// LDS tiles are unchanged.  Offsets in elements; pos - pos % 64 is the block's first position.
+constexpr int KVP_D = 128;
+__host__ __device__ __forceinline__ size_t kc_packed_offset(size_t ctx_index, int pos, int i,
+                                                            int seq_stride) {
+    const int r = pos & 63;
+    const int t = 2 * (r >> 5) + ((r >> 2) & 1), col = 4 * ((r >> 3) & 3) + (r & 3);
+    const int jj = i >> 5, kq = (i >> 3) & 3, e = i & 7;
+    return (ctx_index * seq_stride + (pos - r)) * KVP_D +
+           (size_t)((t * 4 + jj) * 512 + (col + 16 * kq) * 8 + e);
+}
+__host__ __device__ __forceinline__ size_t vc_packed_offset(size_t ctx_index, int pos, int i,
+                                                            int seq_stride) {
+    const int r = pos & 63;
+    const int dt = i >> 4, col = i & 15, j = r >> 5, kq = (r >> 3) & 3, e = r & 7;
+    return (ctx_index * seq_stride + (pos - r)) * KVP_D +
+           (size_t)((dt * 2 + j) * 512 + (col + 16 * kq) * 8 + e);
+}
+
 // Activation layout of the few-row (decode) GEMMs.  pack == 0: plain row-major [m][ld].
 // pack = P > 0 (a power of two >= the row count, at most 64): the values are stored in the
 // order the weight-streaming GEMM feeds them to its 16x16x32 MFMAs, so that each of its
@@ -107,6 +134,7 @@ struct EpiSwiGLU {
 //   kc  : this layer's K cache [max_batch][G][seq_stride][d]
 //   vc  : this layer's V cache, transposed within blocks of 64 positions:
 //         [max_batch][G][seq_stride/64][d][64] (see VT_BLOCK)
+//   (with `packed`, both caches in the packed layout above: kc_packed_offset, vc_packed_offset)
 //   rope: [max_seq][d/2] of (cos, sin)
 template <typename T>
 struct EpiQKV {
@@ -115,6 +143,7 @@ struct EpiQKV {
     int Nq, Nk, d, S, start_pos, G, seq_stride;
     const int* pos_dev;  // if set, the start positions are read from device memory (seq_pos)
     int pos_stride, max_pos;
+    int packed;          // caches in the packed layout (bf16, head_dim 128, matrix-core path)
 
     __device__ __forceinline__ void operator()(int m, int n, float v[4]) const {
         const int b = m / S;
@@ -136,12 +165,22 @@ struct EpiQKV {
         } else if (!write_cache) {
         } else if (n < Nq + Nk) {
             const int nk = n - Nq, g = nk / d, j = nk - g * d;
-            store4(kc + (((size_t)b * G + g) * seq_stride + pos) * d + j, v);
+            const size_t ctx = (size_t)b * G + g;
+            // j % 4 == 0: the four values are contiguous in either layout
+            store4(kc + (packed ? kc_packed_offset(ctx, pos, j, seq_stride)
+                                : (ctx * seq_stride + pos) * d + j), v);
         } else {
             const int nv = n - Nq - Nk, g = nv / d, j = nv - g * d;
-            T* base = vc + vt_offset((size_t)b * G + g, pos, j, d, seq_stride);
+            const size_t ctx = (size_t)b * G + g;
+            if (packed) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) base[(size_t)i * VT_BLOCK] = from_f32<T>(v[i]);
+                for (int i = 0; i < 4; ++i)
+                    vc[vc_packed_offset(ctx, pos, j + i, seq_stride)] = from_f32<T>(v[i]);
+            } else {
+                T* base = vc + vt_offset(ctx, pos, j, d, seq_stride);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) base[(size_t)i * VT_BLOCK] = from_f32<T>(v[i]);
+            }
         }
     }
 };

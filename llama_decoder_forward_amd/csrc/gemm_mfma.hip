@@ -333,7 +333,7 @@ hipError_t gemm_swiglu(Dt dt, const GemmArgs<void>& g, void* out, int ld, int ou
 hipError_t gemm_qkv(Dt dt, const GemmArgs<void>& g, const EpiQKV<void>& e, hipStream_t s) {
     if (dt == Dt::F32) return simt_qkv(g, e, s);
     EpiQKV<bf16> eb{(bf16*)e.q, (bf16*)e.kc, (bf16*)e.vc, e.rope, e.Nq, e.Nk, e.d, e.S,
-                    e.start_pos, e.G, e.seq_stride, e.pos_dev, e.pos_stride, e.max_pos};
+                    e.start_pos, e.G, e.seq_stride, e.pos_dev, e.pos_stride, e.max_pos, e.packed};
     return launch<false>(g, eb, s);
 }
 

@@ -88,8 +88,9 @@ hipError_t simt_swiglu(const GemmArgs<void>& g, void* out, int ld, hipStream_t s
     return launch<float, true>(g, EpiSwiGLU<float>{(float*)out, ld}, s);
 }
 hipError_t simt_qkv(const GemmArgs<void>& g, const EpiQKV<void>& e, hipStream_t s) {
+    // fp32 caches always keep the plain layouts (the packed one is bf16-only)
     EpiQKV<float> ef{(float*)e.q, (float*)e.kc, (float*)e.vc, e.rope, e.Nq, e.Nk, e.d, e.S,
-                     e.start_pos, e.G, e.seq_stride, e.pos_dev, e.pos_stride, e.max_pos};
+                     e.start_pos, e.G, e.seq_stride, e.pos_dev, e.pos_stride, e.max_pos, 0};
     return launch<float, false>(g, ef, s);
 }
 

@@ -96,6 +96,9 @@ struct AttnArgs {
     float* partials; // decode split-K scratch
     int max_ctx;     // upper bound of start_pos + S (sizing of decode grids)
 };
+// The KV cache of a model with these shapes uses the packed layout (kc_packed_offset,
+// vc_packed_offset): exactly when its attention runs on the bf16 matrix-core kernels.
+bool kv_cache_packed(Dt dt, int H, int G, int d);
 hipError_t attention_prefill(Dt dt, const AttnArgs& a, hipStream_t s);
 hipError_t attention_decode(Dt dt, const AttnArgs& a, hipStream_t s);
 // bytes of decode split partials (AttnArgs::partials) for B sequences of H heads
