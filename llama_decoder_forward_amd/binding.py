@@ -302,10 +302,10 @@ class Model:
         raw = self.kv[base:base + n * es].view(self._elem())
         if not self.kv_packed():
             return raw.view(c.max_batch, c.n_kv_heads, self.seq_stride, c.head_dim)
-        # packed: within a 64-position block, [t/2][t%2][jj][kq][col/4][col%4][e] holds key
+        # packed: within a 64-position block, [t/2][t%2][jj][col/4][kq][col%4][e] holds key
         # r = 32 (t/2) + 8 (col/4) + 4 (t%2) + col%4, dimension 32 jj + 8 kq + e
         blk = raw.view(c.max_batch, c.n_kv_heads, self.seq_stride // 64, 2, 2, 4, 4, 4, 4, 8)
-        return blk.permute(0, 1, 2, 3, 7, 4, 8, 5, 6, 9).reshape(
+        return blk.permute(0, 1, 2, 3, 6, 4, 8, 5, 7, 9).reshape(
             c.max_batch, c.n_kv_heads, self.seq_stride, c.head_dim)
 
     def cache_v(self, layer: int) -> torch.Tensor:

@@ -249,16 +249,17 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     //
     // Addressing is kept off the vector ALU: copy i of a wave moves key rows kr = 16 i + 4 wv
     // + lane / 16 and d rows 32 i + 8 wv + lane / 8, whose swizzles do not depend on i.  In
-    // the packed layout key row kr, chunk c sits at run (2 (i / 2) + wv % 2) * 4 + c / 4, lane
-    // 8 (i % 2) + 4 (wv / 2) + lane / 16 + 16 (c % 4); d row dr, chunk c at run (2 i + wv / 2)
-    // * 2 + c / 4, lane 8 (wv % 2) + lane / 8 + 16 (c % 4).  So one per-lane byte offset
-    // serves all four copies of each tile, and the block and copy parts of the address
-    // (8192 (i / 2) + 128 (i % 2) bytes for K, 4096 i for V) are scalar.
+    // the packed layout key row kr, chunk c sits in run (2 (i / 2) + wv % 2) * 4 + c / 4 at
+    // 16-byte position 16 (2 (i % 2) + wv / 2) + 4 (c % 4) + lane / 16; d row dr, chunk c in
+    // run (2 i + wv / 2) * 2 + c / 4 at position 8 (wv % 2) + lane / 8 + 16 (c % 4).  So one
+    // per-lane byte offset serves all four copies of each tile, the block and copy parts of
+    // the address (8192 (i / 2) + 512 (i % 2) bytes for K, 4096 i for V) are scalar, and each
+    // copy reads 8 whole 128-byte lines.
     const int wv = __builtin_amdgcn_readfirstlane(t >> 6);   // the wave index, in a scalar
     const unsigned lds0 = lds_addr(fa_smem);
     const int kc_ = (lane & 15) ^ ((4 * wv + (lane >> 4)) & 15);
-    const unsigned koff = (unsigned)(2 * (((wv & 1) * 4 + (kc_ >> 2)) * 512 +
-                                          (4 * (wv >> 1) + (lane >> 4) + 16 * (kc_ & 3)) * 8));
+    const unsigned koff = (unsigned)(((wv & 1) * 4 + (kc_ >> 2)) * 1024 +
+                                     (16 * (wv >> 1) + 4 * (kc_ & 3) + (lane >> 4)) * 16);
     const int vc_ = (lane & 7) ^ ((4 * wv + (lane >> 4)) & 7);
     const unsigned voff = (unsigned)(2 * (((wv >> 1) * 2 + (vc_ >> 2)) * 512 +
                                           (8 * (wv & 1) + (lane >> 3) + 16 * (vc_ & 3)) * 8));
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
         const unsigned dst = lds0 + st * FA_STAGE_BYTES + wv * 1024;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            lds_dma16_s(ksrc + (i >> 1) * 8192 + (i & 1) * 128, koff, dst + i * 4096);
+            lds_dma16_s(ksrc + (i >> 1) * 8192 + (i & 1) * 512, koff, dst + i * 4096);
 #pragma unroll
         for (int i = 0; i < 4; ++i) lds_dma16_s(vsrc + i * 4096, voff, dst + FA_KBYTES + i * 4096);
     };
@@ -463,7 +464,8 @@ __global__ __launch_bounds__(NWV * 64) void attn_decode_mfma_kernel(
         // kb is a multiple of 64: the block is 16 contiguous 1 KB runs of K and of V^T in the
         // packed layout, run t * 4 + jj of K and dt * 2 + j of V^T being the operand of one load
         u32x4 kr[4][4], vr[8][2];
-        const char* kblk = reinterpret_cast<const char*>(kbase + (size_t)kb * FA_D) + lane * 16;
+        const char* kblk = reinterpret_cast<const char*>(kbase + (size_t)kb * FA_D) +
+                           (16 * (col >> 2) + 4 * kq + (col & 3)) * 16;
         const char* vblk = reinterpret_cast<const char*>(vbase + (size_t)kb * FA_D) + lane * 16;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {

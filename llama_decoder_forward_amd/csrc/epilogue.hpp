@@ -19,8 +19,11 @@ __host__ __device__ __forceinline__ size_t vt_offset(size_t ctx_index, int pos, 
 // 64 positions of one (sequence, KV head) context keeps the same 8192-element place as in the
 // plain layouts, but is ordered as the decode attention loads it: sixteen runs of 1 KB, each
 // the operand of one 16-byte-per-lane load, so that every load is one contiguous 1 KB run.
-//  - K: run t * 4 + jj holds, at lane l = col + 16 kq, the 8 values d = 32 jj + 8 kq .. of
-//    key r = 32 (t / 2) + 8 (col / 4) + 4 (t % 2) + col % 4 of the block;
+//  - K: run t * 4 + jj holds, at 16-byte position 16 (col / 4) + 4 kq + col % 4, the 8 values
+//    d = 32 jj + 8 kq .. of key r = 32 (t / 2) + 8 (col / 4) + 4 (t % 2) + col % 4 of the
+//    block (the decode load of lane col + 16 kq reads that position; the order within the run
+//    puts the 16 pieces of four consecutive keys in one 256-byte span, so that a prefill copy
+//    of four key rows reads whole cache lines);
 //  - V: run dt * 2 + j holds, at lane l = col + 16 kq, the values of dimension d = 16 dt + col
 //    for keys r = 32 j + 8 kq .. +7 of the block.
 // The prefill attention's direct global -> LDS copies address the same 16-byte pieces, so its
@@ -32,7 +35,7 @@ __host__ __device__ __forceinline__ size_t kc_packed_offset(size_t ctx_index, in
     const int t = 2 * (r >> 5) + ((r >> 2) & 1), col = 4 * ((r >> 3) & 3) + (r & 3);
     const int jj = i >> 5, kq = (i >> 3) & 3, e = i & 7;
     return (ctx_index * seq_stride + (pos - r)) * KVP_D +
-           (size_t)((t * 4 + jj) * 512 + (col + 16 * kq) * 8 + e);
+           (size_t)((t * 4 + jj) * 512 + (16 * (col >> 2) + 4 * kq + (col & 3)) * 8 + e);
 }
 __host__ __device__ __forceinline__ size_t vc_packed_offset(size_t ctx_index, int pos, int i,
                                                             int seq_stride) {
