@@ -479,8 +479,7 @@ __global__ __launch_bounds__(NWV * 64) void attn_decode_mfma_kernel(
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int key = kb + 32 * j + 8 * kq;
-                const u32x4 v = (key < c1) ? load_stream16(vblk + (dt * 2 + j) * 1024) : u32x4{0, 0, 0, 0};
-                vr[dt][j] = mask_keys8(v, key, c1);
+                vr[dt][j] = (key < c1) ? load_stream16(vblk + (dt * 2 + j) * 1024) : u32x4{0, 0, 0, 0};
             }
         }
         f32x4 sacc[4];
@@ -524,13 +523,16 @@ __global__ __launch_bounds__(NWV * 64) void attn_decode_mfma_kernel(
         psum += __shfl_xor(psum, 32, 64);
         l_run = l_run * corr + psum;
         m_run = m_new;
+        // the V^T keys past the context are zeroed here, after the S^T MFMAs, so that those
+        // need not wait for the V^T loads (batch 4, context 8200: 31.7 -> 30.2 us on MI355X)
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             oacc[dt] *= corr;
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, vr[dt][j]), pf[j], oacc[dt], 0, 0, 0);
+                    __builtin_bit_cast(bf16x8, mask_keys8(vr[dt][j], kb + 32 * j + 8 * kq, c1)),
+                    pf[j], oacc[dt], 0, 0, 0);
         }
     }
 
