@@ -162,7 +162,10 @@ __device__ __forceinline__ void fa_tile_init(FaTile& T, int blk, int r, int g, i
 // O and l to its new maximum (a wave-uniform branch; O lives in accumulation registers and a
 // rescale costs three instructions per element).  Otherwise p <= 2^8, well inside bf16 and
 // fp32 range.  O and l share the reference, so O / l is the softmax-weighted sum.
+// EMPTY_ROWS: the block may hold rows that have seen no unmasked key yet, in this block or
+// before it (a workgroup's second set of key blocks, which does not start at key 0).
 constexpr float FA_RESCALE_SLACK = 8.0f;
+template <bool EMPTY_ROWS>
 __device__ __forceinline__ void fa_softmax(FaTile& T, f32x16 (&sacc)[2], bf16x8 (&pf)[4], int kv0,
                                            int lh, float scale_log2) {
     if (kv0 + FA_BKV - 1 > T.p_lo) {  // the block reaches past some row's own position
@@ -182,7 +185,9 @@ __device__ __forceinline__ void fa_softmax(FaTile& T, f32x16 (&sacc)[2], bf16x8 
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
     if (__builtin_amdgcn_ballot_w64(mx > T.m + FA_RESCALE_SLACK) != 0) {
         const float m_new = fmaxf(T.m, mx);
-        const float corr = __builtin_amdgcn_exp2f(T.m - m_new);  // 0 while T.m = -inf
+        // 0 while T.m = -inf (O = 0, l = 0): with EMPTY_ROWS also where the row's new
+        // maximum is still -inf
+        const float corr = EMPTY_ROWS && T.m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(T.m - m_new);
         T.l *= corr;
         // in groups of 8, so that few registers hold values on their way back
 #pragma unroll
@@ -195,12 +200,16 @@ __device__ __forceinline__ void fa_softmax(FaTile& T, f32x16 (&sacc)[2], bf16x8 
             }
         T.m = m_new;
     }
+    // With EMPTY_ROWS a row whose keys so far were all masked still has T.m = -inf; its
+    // exponentials are then taken against 0, so that masked keys give 0 rather than
+    // 2^(-inf + inf).
+    const float msub = EMPTY_ROWS && T.m == -INFINITY ? 0.0f : T.m;
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[i][e], scale_log2, -T.m));
+            const float p = __builtin_amdgcn_exp2f(fmaf(sacc[i][e], scale_log2, -msub));
             psum += p;
             sacc[i][e] = p;
         }
@@ -212,27 +221,48 @@ __device__ __forceinline__ void fa_softmax(FaTile& T, f32x16 (&sacc)[2], bf16x8 
 }
 
 // Workgroup = (sequence b, KV head g, query block qb): BQ = 128/group positions for the
-// group's query heads, 128 query rows; wave w owns rows 32w..32w+31 as one query tile.  Two
-// workgroups share a CU (64 KB of LDS each), so each SIMD runs two waves and one wave's
-// softmax overlaps the other's MFMAs.  Grid order: the first half of the workgroups take
-// the late (long) query blocks, latest first, the second half the matching early ones, so
-// that the two workgroups of a CU together cover about the same number of key blocks.
-__global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
+// group's query heads, 128 query rows; wave w of a 4-wave set owns rows 32w..32w+31 as one
+// query tile.
+//
+// NH = 1: one 4-wave set takes every key block; two workgroups share a CU (64 KB of LDS
+// each), so each SIMD runs two waves and one wave's softmax overlaps the other's MFMAs.
+// Grid order: the first half of the workgroups take the late (long) query blocks, latest
+// first, the second half the matching early ones.
+//
+// NH = 2: two 4-wave sets over the same 128 query rows, set h taking key blocks h, h + 2,
+// h + 4, ..; each set has its own double buffer (128 KB, one workgroup per CU), and set 1
+// hands its softmax state (max, sum, unnormalised O) to set 0 through LDS at the end, where
+// the two partial softmaxes merge exactly as the online softmax merges two key blocks.
+// Wave w of each set runs on SIMD w, so every SIMD again holds two waves with the same
+// work.  The grid runs latest query block first: a CU that finishes a short block takes
+// the next longest one, so every CU ends up with about the same number of key blocks.
+// This is for grids of about one round of workgroups (2048 tokens), where with NH = 1 the
+// CU that holds the longest query block runs it alone at one wave per SIMD once its short
+// partner has finished.
+template <int NH>
+__global__ __launch_bounds__(256 * NH, 2 / NH) void attn_prefill_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
     bf16* __restrict__ out, int S, int start_pos, int H, int G, int seq_stride,
     float scale_log2, int nqb, int out_pack) {
+    static_assert(NH == 1 || NH == 2, "one or two key-block sets");
     extern __shared__ u32x4 fa_smem[];
     const int group = H / G, BQ = FA_ROWS / group;
     const int GB = G * (gridDim.x / (nqb * G));  // (b, g) pairs
-    const int heavy = (nqb + 1) / 2;             // blocks nqb-1 .. nqb-heavy come first
     const int idx = (int)blockIdx.x;
-    const int qb = idx < heavy * GB ? nqb - 1 - idx / GB : (idx - heavy * GB) / GB;
+    int qb;
+    if constexpr (NH == 1) {
+        const int heavy = (nqb + 1) / 2;         // blocks nqb-1 .. nqb-heavy come first
+        qb = idx < heavy * GB ? nqb - 1 - idx / GB : (idx - heavy * GB) / GB;
+    } else {
+        qb = nqb - 1 - idx / GB;
+    }
     const int gb = idx % GB;
     const int b = gb / G, g = gb % G;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, lr = lane & 31, lh = lane >> 5;
+    const int wq = wave & 3;                     // the wave's query tile within its set
 
     FaTile T;
-    fa_tile_init(T, qb, wave * 32 + lr, g, S, start_pos, group, BQ);
+    fa_tile_init(T, qb, wq * 32 + lr, g, S, start_pos, group, BQ);
     const int nkb = T.nkb;
 
     const bf16* kbase = kc + ((size_t)b * G + g) * seq_stride * FA_D;
@@ -245,7 +275,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     // (kc_packed_offset, vc_packed_offset); both operand reads below are conflict-free
     // 16-byte reads.  Keys past the sequence's context are read too (whole 64-position
     // blocks inside the cache); the causal mask gives them probability 0 and the cache holds
-    // finite values.
+    // finite values.  Set h of the workgroup owns the two stage buffers at 2 h STAGE.
     //
     // Addressing is kept off the vector ALU: copy i of a wave moves key rows kr = 16 i + 4 wv
     // + lane / 16 and d rows 32 i + 8 wv + lane / 8, whose swizzles do not depend on i.  In
@@ -255,8 +285,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     // per-lane byte offset serves all four copies of each tile, the block and copy parts of
     // the address (8192 (i / 2) + 512 (i % 2) bytes for K, 4096 i for V) are scalar, and each
     // copy reads 8 whole 128-byte lines.
-    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);   // the wave index, in a scalar
+    const int wv = __builtin_amdgcn_readfirstlane(wq);      // the wave index in its set, scalar
+    const int set = NH == 1 ? 0 : __builtin_amdgcn_readfirstlane(wave >> 2);
     const unsigned lds0 = lds_addr(fa_smem);
+    const unsigned set0 = lds0 + set * 2 * FA_STAGE_BYTES;
     const int kc_ = (lane & 15) ^ ((4 * wv + (lane >> 4)) & 15);
     const unsigned koff = (unsigned)(((wv & 1) * 4 + (kc_ >> 2)) * 1024 +
                                      (16 * (wv >> 1) + 4 * (kc_ & 3) + (lane >> 4)) * 16);
@@ -266,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     auto issue = [&](int st, int kb) {
         const char* ksrc = reinterpret_cast<const char*>(kbase + (size_t)kb * FA_BKV * FA_D);
         const char* vsrc = reinterpret_cast<const char*>(vbase + (size_t)kb * FA_D * VT_BLOCK);
-        const unsigned dst = lds0 + st * FA_STAGE_BYTES + wv * 1024;
+        const unsigned dst = set0 + st * FA_STAGE_BYTES + wv * 1024;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             lds_dma16_s(ksrc + (i >> 1) * 8192 + (i & 1) * 512, koff, dst + i * 4096);
@@ -274,23 +306,23 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
         for (int i = 0; i < 4; ++i) lds_dma16_s(vsrc + i * 4096, voff, dst + FA_KBYTES + i * 4096);
     };
 
-    // The query tile arrives through the second stage buffer by the same direct copies (each
-    // 1 KB copy = 4 whole rows, so every global read is a full 256-byte row segment; rows
-    // past the call's tokens read its last token and are never stored), while the first
-    // key block lands in the first buffer.
-    issue(0, 0);
+    // The query tile arrives through set 0's second stage buffer by the same direct copies
+    // (each 1 KB copy = 4 whole rows, so every global read is a full 256-byte row segment;
+    // rows past the call's tokens read its last token and are never stored), while each
+    // set's first key block lands in its first buffer.
+    if (set < nkb) issue(0, set);
     {
         const unsigned qdst = lds0 + FA_STAGE_BYTES;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int ci = wave + 4 * i;
+        for (int i = 0; i < 8 / NH; ++i) {
+            const int ci = wave + 4 * NH * i;
             const int qr = 4 * ci + (lane >> 4), slot = lane & 15;
             const int sq = min(qb * BQ + qr % BQ, S - 1);
             const bf16* qsrc = q + ((size_t)(b * S + sq) * H + g * group + qr / BQ) * FA_D;
             lds_dma16(qsrc + ((slot ^ (qr & 15)) * 8), qdst + ci * 1024);
         }
         wait_copies_and_barrier();
-        const int r = wave * 32 + lr;
+        const int r = wq * 32 + lr;
         const u32x4* qs = fa_smem + FA_STAGE_BYTES / 16;
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
@@ -307,14 +339,20 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     // + lr, at (va ^ 32j) + 4096 td.  The stage offset is a compile-time constant of each
     // of the loop's two unrolled halves, so every read is one XOR and an immediate offset.
     const int krow = 16 * (lr >> 4) + 8 * ((lr >> 2) & 1) + 4 * ((lr >> 3) & 1) + (lr & 3);
-    const unsigned ka = (unsigned)(krow * 256 + ((lh ^ (krow & 15)) * 16));
-    const unsigned va = (unsigned)(lr * 128 + ((lh ^ ((lr >> 1) & 7)) * 16));
+    // (the set's buffer offset, a multiple of 64 KB, is part of the per-lane address and
+    // leaves the XOR bits alone)
+    const unsigned ka = (unsigned)(krow * 256 + ((lh ^ (krow & 15)) * 16) + set * 2 * FA_STAGE_BYTES);
+    const unsigned va = (unsigned)(lr * 128 + ((lh ^ ((lr >> 1) & 7)) * 16) + set * 2 * FA_STAGE_BYTES);
     const char* lds_c = reinterpret_cast<const char*>(fa_smem);
-    auto block = [&](int kb, auto st_c) {
+    // Step j of the loop: the set's key block kb = NH j + set.  Both sets pass the same
+    // number of barriers; set 1 skips the work of a step past the last block (odd nkb).
+    auto block = [&](int j, auto st_c) {
         constexpr int st = decltype(st_c)::value;
+        const int kb = NH * j + set;
         // block kb has landed, and every wave's reads of the other slot have returned
         wait_copies_and_barrier();
-        if (kb + 1 < nkb) issue(st ^ 1, kb + 1);
+        if (kb + NH < nkb) issue(st ^ 1, kb + NH);
+        if (kb >= nkb) return;
         const int kv0 = kb * FA_BKV;
         f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -335,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
                     sacc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[k2][i], T.qf[2 * h + k2], sacc[i], 0, 0, 0);
         }
         bf16x8 pf[4];
-        fa_softmax(T, sacc, pf, kv0, lh, scale_log2);
+        fa_softmax<NH == 2>(T, sacc, pf, kv0, lh, scale_log2);
         // O^T += V^T P^T: the V^T operand of k-step j for lane lh is keys 16j + 8lh .. +7 of
         // row d, the 16-byte chunk 2j + lh
 #pragma unroll
@@ -350,21 +388,59 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
                 T.o[td] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pf[j], T.o[td], 0, 0, 0);
         }
     };
-    int kb = 0;
-    for (; kb + 1 < nkb; kb += 2) {
-        block(kb, std::integral_constant<int, 0>{});
-        block(kb + 1, std::integral_constant<int, 1>{});
+    const int nsteps = (nkb + NH - 1) / NH;
+    int j = 0;
+    for (; j + 1 < nsteps; j += 2) {
+        block(j, std::integral_constant<int, 0>{});
+        block(j + 1, std::integral_constant<int, 1>{});
     }
-    if (kb < nkb) block(kb, std::integral_constant<int, 0>{});
+    if (j < nsteps) block(j, std::integral_constant<int, 0>{});
+
+    // every wave is past its last key block and its LDS reads have returned
+    wait_lgkm_and_barrier();
+    if constexpr (NH == 2) {
+        // Set 1's state leaves through LDS in lane order (each store one contiguous 1 KB):
+        // O^T tile td, registers 4c..4c+3 at ((wq 4 + td) 4 + c) KB + 16 lane, then (m, l)
+        // at 64 KB + 512 wq + 8 lane.  Set 0 merges it into its own:
+        //   m = max(m0, m1), O = O0 2^(m0 - m) + O1 2^(m1 - m), l likewise,
+        // with set 1's state empty (m = -inf, l = 0, O = 0) when it saw no key block.
+        char* sb = reinterpret_cast<char*>(fa_smem);
+        if (set == 1) {
+#pragma unroll
+            for (int td = 0; td < 4; ++td)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    *reinterpret_cast<f32x4*>(sb + ((wq * 4 + td) * 4 + c) * 1024 + lane * 16) =
+                        f32x4{T.o[td][4 * c], T.o[td][4 * c + 1], T.o[td][4 * c + 2], T.o[td][4 * c + 3]};
+            *reinterpret_cast<float2*>(sb + 65536 + wq * 512 + lane * 8) = float2{T.m, T.l};
+        }
+        wait_lgkm_and_barrier();
+        if (set == 0) {
+            const float2 ml = *reinterpret_cast<const float2*>(sb + 65536 + wq * 512 + lane * 8);
+            const float m_new = fmaxf(T.m, ml.x);
+            const float c0 = __builtin_amdgcn_exp2f(T.m - m_new);
+            const float c1 = __builtin_amdgcn_exp2f(ml.x - m_new);
+            T.l = T.l * c0 + ml.y * c1;
+#pragma unroll
+            for (int td = 0; td < 4; ++td)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const f32x4 o1 = *reinterpret_cast<const f32x4*>(sb + ((wq * 4 + td) * 4 + c) * 1024 + lane * 16);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) T.o[td][4 * c + e] = T.o[td][4 * c + e] * c0 + o1[e] * c1;
+                }
+        }
+    }
 
     // The normalised output goes through LDS (the first stage buffer, free once every wave
-    // is past its last key block) and leaves as whole 16-byte chunks of each row: lane
-    // (lr, lh) holds d = 32 td + 8 gg + 4 lh .. +3 of its row, half of chunk 4 td + gg.
-    wait_lgkm_and_barrier();
-    {
+    // is past its last key block; with two sets the last 32 KB, clear of set 1's state) and
+    // leaves as whole 16-byte chunks of each row: lane (lr, lh) holds d = 32 td + 8 gg + 4 lh
+    // .. +3 of its row, half of chunk 4 td + gg.
+    constexpr int OUT0 = NH == 2 ? 3 * FA_STAGE_BYTES : 0;
+    if (set == 0) {
         const float inv = 1.0f / T.l;
-        const int r = wave * 32 + lr;
-        char* ob = reinterpret_cast<char*>(fa_smem);
+        const int r = wq * 32 + lr;
+        char* ob = reinterpret_cast<char*>(fa_smem) + OUT0;
 #pragma unroll
         for (int td = 0; td < 4; ++td)
 #pragma unroll
@@ -376,32 +452,47 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
             }
     }
     wait_lgkm_and_barrier();
+    const u32x4* os = fa_smem + OUT0 / 16;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int ch = i * 256 + t, r = ch >> 4, c = ch & 15;
+    for (int i = 0; i < 8 / NH; ++i) {
+        const int ch = i * 256 * NH + t, r = ch >> 4, c = ch & 15;
         const int sq = qb * BQ + r % BQ;
         if (sq < S) {
-            const u32x4 v = fa_smem[r * 16 + (c ^ (r & 15))];
+            const u32x4 v = os[r * 16 + (c ^ (r & 15))];
             *reinterpret_cast<u32x4*>(out + act_offset(b * S + sq, (g * group + r / BQ) * FA_D + c * 8,
                                                        H * FA_D, out_pack)) = v;
         }
     }
 }
 
+template <int NH>
+hipError_t launch_prefill_nh(const AttnArgs& a, int nqb, float scale_log2, hipStream_t s) {
+    static PerDevice attr;
+    hipError_t e = attr.once([](int) {
+        return hipFuncSetAttribute((const void*)attn_prefill_mfma_kernel<NH>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize,
+                                   (int)(2 * NH * FA_STAGE_BYTES));
+    });
+    if (e != hipSuccess) return e;
+    attn_prefill_mfma_kernel<NH><<<nqb * a.G * a.B, 256 * NH, 2 * NH * FA_STAGE_BYTES, s>>>(
+        (const bf16*)a.q, (const bf16*)a.kc, (const bf16*)a.vc, (bf16*)a.out, a.S, a.start_pos,
+        a.H, a.G, a.seq_stride, scale_log2, nqb, a.out_pack);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_mfma(const AttnArgs& a, hipStream_t s) {
     const int group = a.H / a.G, BQ = FA_ROWS / group;
     const int nqb = (a.S + BQ - 1) / BQ;
     const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_D);
-    static PerDevice attr;
-    hipError_t e = attr.once([](int) {
-        return hipFuncSetAttribute((const void*)attn_prefill_mfma_kernel,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)(2 * FA_STAGE_BYTES));
-    });
-    if (e != hipSuccess) return e;
-    attn_prefill_mfma_kernel<<<nqb * a.G * a.B, 256, 2 * FA_STAGE_BYTES, s>>>(
-        (const bf16*)a.q, (const bf16*)a.kc, (const bf16*)a.vc, (bf16*)a.out, a.S, a.start_pos,
-        a.H, a.G, a.seq_stride, scale_log2, nqb, a.out_pack);
-    return hipGetLastError();
+    // Two key-block sets per workgroup while the grid is at most about two rounds of one
+    // workgroup per CU and the query blocks' key counts differ widely (the call starts
+    // within one chunk of position 0, so that its last block reads at least twice the keys
+    // of its first).  A chunk far into a sequence (start_pos >= S) has blocks of nearly
+    // equal length, which two 4-wave workgroups per CU run better (measured on MI355X,
+    // 2048 tokens after a 2048-token prefix).
+    if ((long)nqb * a.G * a.B <= 2L * cu_count() && a.S >= a.start_pos + 2 * BQ)
+        return launch_prefill_nh<2>(a, nqb, scale_log2, s);
+    return launch_prefill_nh<1>(a, nqb, scale_log2, s);
 }
 
 // ------------------------------------------------------------------------------------

@@ -27,6 +27,9 @@ struct PerDevice {
     }
 };
 
+// Compute units of the current device (gemm_skinny.hip); 256 if it cannot be queried.
+int cu_count();
+
 // ---- elementwise / reductions (elementwise.hip)
 hipError_t rope_table(float2* rope, int max_seq, int d, float theta, hipStream_t s);
 hipError_t embed(Dt dt, const int* tokens, const void* E, float* x, int rows, int D, int V,

@@ -58,6 +58,16 @@ def test_bf16_prefill_at_chunks():
     _chunks_vs_oracle(small_bf16_spec(), 12, 2, ((0, 70), (70, 130), (130, 131)), BF16_TOL, 160)
 
 
+def test_bf16_prefill_at_chunks_inside_a_key_block():
+    # four query heads per KV head (32 positions per query tile) and chunks that start
+    # inside a 64-key block: a chunk's first query tile then meets a key block whose keys
+    # all lie past the positions of some of its rows, with no earlier key seen by those
+    # rows in the same pass (the case the exponentials must take against 0, not -inf)
+    say("bf16 stack, 8 query heads / 2 KV heads: prefill of 130 tokens as chunks 40 + 32 + 58, B=2")
+    spec = small_bf16_spec(dim=1024, n_heads=8, n_kv_heads=2)
+    _chunks_vs_oracle(spec, 13, 2, ((0, 40), (40, 72), (72, 130)), BF16_TOL, 160)
+
+
 def _ragged_vs_oracle(spec, seed, B, S, positions, steps, tol, max_seq):
     m, synth = build_model(spec, seed, max_batch=B, max_seq=max_seq, max_tokens=B * S)
     toks = syn.tokens(seed, B, S, spec.vocab_size)
