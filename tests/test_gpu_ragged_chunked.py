@@ -68,6 +68,15 @@ def test_bf16_prefill_at_chunks_inside_a_key_block():
     _chunks_vs_oracle(spec, 13, 2, ((0, 40), (40, 72), (72, 130)), BF16_TOL, 160)
 
 
+@pytest.mark.parametrize("H,G", [(16, 2), (16, 1)])
+def test_bf16_prefill_at_chunks_wide_groups(H, G):
+    # 8 and 16 query heads per KV head (16 and 8 positions per 128-row query tile), from
+    # position 0 and from a start inside a key block
+    say(f"bf16 stack, {H} query heads / {G} KV heads: prefill of 150 tokens as chunks 37 + 113, B=2")
+    spec = small_bf16_spec(dim=128 * H, n_heads=H, n_kv_heads=G)
+    _chunks_vs_oracle(spec, 14, 2, ((0, 37), (37, 150)), BF16_TOL, 160)
+
+
 def _ragged_vs_oracle(spec, seed, B, S, positions, steps, tol, max_seq):
     m, synth = build_model(spec, seed, max_batch=B, max_seq=max_seq, max_tokens=B * S)
     toks = syn.tokens(seed, B, S, spec.vocab_size)
