@@ -107,7 +107,8 @@ size_t llama_kv_cache_bytes(const llama_config *cfg);
 /* Bytes of device workspace the caller must provide for this config: the activations of
  * up to max(max_tokens, max_batch) rows between the steps of the article's layer (sections
  * 构建Transformer层 to 前馈神经网络层), the rotary table of section 位置编码, attention
- * partials, split-K sums of the few-row GEMMs, device flags.  The largest call is fixed by
+ * partials, split-K sums of the residual GEMMs (the few-row ones, and the down projection of
+ * a prefill of up to 4096 rows), device flags.  The largest call is fixed by
  * the config's max_tokens, so the size depends on the config alone.  0 if the config is
  * invalid. */
 size_t llama_workspace_bytes(const llama_config *cfg);

@@ -56,8 +56,10 @@ Layout layout_of(const llama_config& c) {
     L.g = take(arows * (size_t)c.ffn_hidden * es);
     L.logits = take((size_t)c.max_batch * c.vocab_size * 4);
     L.partials = take(lk::decode_partials_bytes(c.max_batch, c.n_heads, c.head_dim, seq_stride_of(c)));
-    // split-K sums of the residual GEMMs on the few-row path (at most 64 rows)
-    L.kpart = take((size_t)lk::LLAMA_MAX_KSPLITS * 64 * D * 4);
+    // split-K sums of the residual GEMMs: on the few-row path (at most 64 rows) and on the
+    // tiled path (two splits of at most LLAMA_TILED_SPLIT_MAX_ROWS rows)
+    L.kpart = take(std::max((size_t)lk::LLAMA_MAX_KSPLITS * 64 * D * 4,
+                            (size_t)2 * std::min<size_t>(rows, lk::LLAMA_TILED_SPLIT_MAX_ROWS) * D * 4));
     L.tokbuf = take((size_t)c.max_batch * 4);
     L.argmax = take(lk::argmax_scratch_bytes(c.max_batch, c.vocab_size));
     L.total = off;
@@ -305,13 +307,24 @@ llama_status run_layer(llama_model* m, int l, const float* xin, float* xout, int
         ProfScope ps(m, LLAMA_KERNEL_FFN_UP, s);
         HIP_TRY(lk::gemm_swiglu(m->dt, ff, m->g(), c.ffn_hidden, pk_down, s));
     }
-    // W2: x_out += g W2, left pending (split over K) when the caller takes pending sums
-    const int w2_splits = pend ? lk::residual_splits(m->dt, T, D, c.ffn_hidden) : 0;
+    // W2: x_out += g W2, left pending (split over K) when the caller takes pending sums.  A
+    // call that takes none (llama_layer_forward) leaves none: on the few-row path its W2 is
+    // not split; on the tiled path the split sums are added at once, by the same fold the
+    // next layer's norm applies, so that its output equals a prefill's layer output bit for
+    // bit (the fold's normalised rows land in the scratch activation buffer, unused).
+    int w2_splits = lk::residual_splits(m->dt, T, D, c.ffn_hidden);
+    const bool fold_now = !pend && w2_splits > 0 && T > 64;
+    if (!pend && !fold_now) w2_splits = 0;
     {
         ProfScope ps(m, LLAMA_KERNEL_FFN_DOWN, s);
         const lk::GemmArgs<void> ga = gemm_args(m, m->g(), c.ffn_hidden, w.w2, T, D, c.ffn_hidden);
         if (w2_splits > 0) HIP_TRY(lk::gemm_residual_split(m->dt, ga, scr.kpart, w2_splits, s));
         else HIP_TRY(lk::gemm_residual(m->dt, ga, EpiResidual{xout, xout, D}, s));
+    }
+    if (fold_now) {
+        ProfScope ps(m, LLAMA_KERNEL_RMSNORM, s);
+        HIP_TRY(lk::rmsnorm_fold(m->dt, xout, scr.kpart, w2_splits, (size_t)T * D, xout, 1, 0,
+                                 w.ffn_norm, m->h(), pk_up, T, D, c.norm_eps, s));
     }
     if (pend) *pend = Pending{w2_splits, (size_t)T * D};
     return LLAMA_OK;

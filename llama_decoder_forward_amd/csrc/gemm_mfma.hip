@@ -77,6 +77,9 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
     const int tile_m = first_m + (bid % per_group) % gsize, tile_n = (bid % per_group) / gsize;
     const int n0 = n_begin + tile_n * BN, m0 = tile_m * BM;
 
+    // split z = blockIdx.y of a split-K launch (the fp32 partial-sum epilogue) takes k in
+    // [z K, z K + K) of the rows; every other launch has one split, compiled without it
+    const int k_off = std::is_same<Epi, EpiPartial>::value ? (int)blockIdx.y * K : 0;
     // this lane's source address for each of its wave's copies of a stage
     const bf16* src[SPW];
 #pragma unroll
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
             const int m = m0 + r - NA * BN;
             p = A + (size_t)(m < M ? m : 0) * lda;   // rows past M / N load row 0, unused
         }
-        src[i] = p + c * 8;
+        src[i] = p + k_off + c * 8;
     }
     f32x16 acc[TN][TM];
     f32x16 acc3[DUAL ? TN : 1][DUAL ? TM : 1];
@@ -241,7 +244,8 @@ __global__ __launch_bounds__(WN * WM * 64) void gemm_mfma_kernel(
 }
 
 template <int BN, int BM, int BK, int WN, int WM, bool DUAL, typename Epi>
-hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s, int n_begin = 0) {
+hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s, int n_begin = 0,
+                      int splits = 1) {
     const WeightRows<bf16> W{(const bf16*)g.W.p0, (const bf16*)g.W.p1, (const bf16*)g.W.p2, g.W.end0, g.W.end1, g.W.ld};
     const WeightRows<bf16> W3{(const bf16*)g.W3.p0, (const bf16*)g.W3.p1, (const bf16*)g.W3.p2, g.W3.end0, g.W3.end1, g.W3.ld};
     constexpr int ROWS = (DUAL ? 2 : 1) * BN + BM;
@@ -263,8 +267,8 @@ hipError_t launch_cfg(const GemmArgs<void>& g, const Epi& e, hipStream_t s, int 
     int group_m = 8;
     if (DUAL) group_m = nt_m <= 8 ? 2 : 4;
     else if (g.K >= 8192 && nt_m > 8) group_m = 2;
-    kern<<<tiles, WN * WM * 64, lds_bytes, s>>>((const bf16*)g.A, g.lda, W, W3, g.M, g.N, g.K,
-                                                n_begin, group_m, e);
+    kern<<<dim3(tiles, splits), WN * WM * 64, lds_bytes, s>>>((const bf16*)g.A, g.lda, W, W3, g.M,
+                                                              g.N, g.K / splits, n_begin, group_m, e);
     return hipGetLastError();
 }
 
@@ -316,6 +320,28 @@ hipError_t launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s) {
 }
 
 }  // namespace
+
+// Split-K form of a residual GEMM with many token rows (the down projection of a prefill of
+// up to a few thousand tokens): 256 x 256 tiles, each of the `splits` k ranges in its own
+// workgroup, writing fp32 sums to part (EpiPartial); the next RMSNorm of the residual stream
+// adds them.  Used where the unsplit 256 x 256 grid would fill at most half the CUs, so that
+// the split grid fills them once: there the alternative is 256 x 128 tiles, whose operand
+// copies per FLOP are a third higher.
+int tiled_residual_splits(Dt dt, int M, int N, int K) {
+    if (dt != Dt::BF16 || M <= 64 || M > LLAMA_TILED_SPLIT_MAX_ROWS || N % 256 != 0 ||
+        K < 8192 || K % 128 != 0)
+        return 0;
+    const long long tiles = (long long)((M + 255) / 256) * (N / 256);
+    return 2 * tiles <= cu_count() ? 2 : 0;
+}
+
+hipError_t gemm_residual_split_tiled(const GemmArgs<void>& g, float* part, int splits,
+                                     hipStream_t s) {
+    if (splits != tiled_residual_splits(Dt::BF16, g.M, g.N, g.K) || g.a_pack != 0)
+        return hipErrorInvalidValue;
+    return launch_cfg<256, 256, 64, 2, 4, false>(g, EpiPartial{part, g.N, (size_t)g.M * g.N}, s,
+                                                 0, splits);
+}
 
 hipError_t gemm_store_f32(Dt dt, const GemmArgs<void>& g, EpiStoreF32 e, hipStream_t s) {
     if (dt == Dt::F32) return simt_store_f32(g, e, s);

@@ -227,6 +227,7 @@ int act_pack(Dt dt, int M, int N, int K) {
 // workgroups instead, to keep every compute unit busy; the splits' sums go to `part` and
 // the next RMSNorm adds them to the residual stream.
 int residual_splits(Dt dt, int M, int N, int K) {
+    if (M > 64) return tiled_residual_splits(dt, M, N, K);
     if (act_pack(dt, M, N, K) == 0 || N % (SK_ROWS * SPLIT_RT) != 0) return 0;
     const int strips = N / (SK_ROWS * SPLIT_RT);
     const int blocks = K / SK_KB;
@@ -238,6 +239,7 @@ int residual_splits(Dt dt, int M, int N, int K) {
 
 hipError_t gemm_residual_split(Dt dt, const GemmArgs<void>& g, float* part, int splits,
                                hipStream_t s) {
+    if (dt == Dt::BF16 && g.M > 64) return gemm_residual_split_tiled(g, part, splits, s);
     if (dt != Dt::BF16 || splits != residual_splits(dt, g.M, g.N, g.K) ||
         g.a_pack != act_pack(dt, g.M, g.N, g.K))
         return hipErrorInvalidValue;

@@ -77,11 +77,17 @@ template <bool DUAL, typename Epi>
 hipError_t skinny_launch(const GemmArgs<void>& g, const Epi& e, hipStream_t s);
 hipError_t gemm_store_f32(Dt dt, const GemmArgs<void>& g, EpiStoreF32 e, hipStream_t s);
 hipError_t gemm_residual(Dt dt, const GemmArgs<void>& g, EpiResidual e, hipStream_t s);
-// Split-K form of a residual GEMM on the weight-streaming path: part[z][m][n] (z < splits,
-// splits = residual_splits(...), split stride M*N floats) holds split z's share of acc; the
-// residual itself is not touched.  residual_splits returns 0 where this form is not used.
+// Split-K form of a residual GEMM: part[z][m][n] (z < splits, splits = residual_splits(...),
+// split stride M*N floats) holds split z's share of acc; the residual itself is not touched.
+// residual_splits returns 0 where this form is not used.  Up to 64 rows it is the
+// weight-streaming path's; beyond, the tiled path's (tiled_residual_splits).
 constexpr int LLAMA_MAX_KSPLITS = 16;
+// Rows up to which a residual GEMM on the tiled path may be split over K (the workspace
+// holds two splits' sums of that many rows).
+constexpr int LLAMA_TILED_SPLIT_MAX_ROWS = 4096;
 int residual_splits(Dt dt, int M, int N, int K);
+int tiled_residual_splits(Dt dt, int M, int N, int K);
+hipError_t gemm_residual_split_tiled(const GemmArgs<void>& g, float* part, int splits, hipStream_t s);
 hipError_t gemm_residual_split(Dt dt, const GemmArgs<void>& g, float* part, int splits, hipStream_t s);
 hipError_t gemm_swiglu(Dt dt, const GemmArgs<void>& g, void* out, int ld, int out_pack, hipStream_t s);
 hipError_t gemm_qkv(Dt dt, const GemmArgs<void>& g, const EpiQKV<void>& e, hipStream_t s);
