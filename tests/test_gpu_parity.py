@@ -369,3 +369,41 @@ def test_trace_records_the_residual_stream():
     assert_rows_close(lg.reshape(B * S, -1), O.head_logits(h[spec.n_layers].astype(np.float64), W, spec),
                       BF16_TOL, "head on the recorded final rows")
     m.sync_status()
+
+
+def test_bf16_split_down_projection():
+    # F = 8192: the down projection of a prefill of more than 64 rows, and of a decode step
+    # of more than 64 sequences, is split over K in two (fp32 sums folded by the next
+    # RMSNorm); the prefill against the oracle, llama_layer_forward against the recorded
+    # residual stream bit for bit (it folds the sums at once), and two teacher-forced decode
+    # steps at batch 80
+    spec = small_bf16_spec(ffn_hidden=8192)
+    B, S, DB, steps = 2, 70, 80, 2
+    say(f"small bf16 stack, F=8192: prefill {B} x {S} with a residual-stream trace, then "
+        f"{steps} decode steps at batch {DB}")
+    m, synth = build_model(spec, 26, max_batch=DB, max_seq=S + steps, max_tokens=DB * S)
+    W = syn.FloatView(synth)
+    toks = syn.tokens(26, B, S, spec.vocab_size)
+    tr = m.trace_hidden(B * S)
+    got = m.prefill(torch.from_numpy(toks).cuda(), all_positions=True).cpu().numpy()
+    h = tr.cpu().numpy()
+    m.trace_hidden(None)
+    ref, _ = O.prefill(toks, W, spec, all_positions=True)
+    assert_rows_close(got, ref, BF16_TOL, "prefill logits")
+    for l in range(spec.n_layers):
+        x_in = torch.from_numpy(np.ascontiguousarray(h[l].reshape(B, S, -1))).cuda()
+        x_out = m.layer_forward(l, x_in).cpu().numpy().reshape(B * S, -1)
+        np.testing.assert_array_equal(x_out, h[l + 1], err_msg=f"layer {l}")
+    dtoks = syn.tokens(27, DB, S, spec.vocab_size)
+    ref0, caches = O.prefill(dtoks, W, spec, capacity=S + steps)
+    got0 = m.prefill(torch.from_numpy(dtoks).cuda()).cpu().numpy()
+    assert_rows_close(got0, ref0, BF16_TOL, "prefill last logits")
+    cur = O.argmax(ref0).astype(np.int32)
+    for k in range(steps):
+        ref = O.decode_step(cur, S + k, W, spec, caches)
+        nxt, lg = m.decode_step(torch.from_numpy(cur).cuda(), S + k)
+        lg = lg.cpu().numpy()
+        assert_rows_close(lg, ref, BF16_TOL, f"decode step {k}")
+        check_argmax(nxt.cpu().numpy(), lg, ref, f"decode step {k}")
+        cur = O.argmax(ref).astype(np.int32)
+    m.sync_status()
