@@ -236,9 +236,10 @@ __device__ __forceinline__ void fa_softmax(FaTile& T, f32x16 (&sacc)[2], bf16x8 
 // Wave w of each set runs on SIMD w, so every SIMD again holds two waves with the same
 // work.  The grid runs latest query block first: a CU that finishes a short block takes
 // the next longest one, so every CU ends up with about the same number of key blocks.
-// This is for grids of about one round of workgroups (2048 tokens), where with NH = 1 the
-// CU that holds the longest query block runs it alone at one wave per SIMD once its short
-// partner has finished.
+// The launcher takes it for grids of at most about two rounds of workgroups whose query
+// blocks differ widely in length (a call from near position 0, e.g. 2048 tokens), where
+// with NH = 1 the CU that holds the longest query block runs it alone at one wave per SIMD
+// once its short partner has finished.
 template <int NH>
 __global__ __launch_bounds__(256 * NH, 2 / NH) void attn_prefill_mfma_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ kc, const bf16* __restrict__ vc,
