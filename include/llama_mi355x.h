@@ -237,9 +237,11 @@ typedef enum {
     LLAMA_KERNEL_NONE = 0,
     LLAMA_KERNEL_QKV = 1,        /* Q/K/V projection with RoPE and cache write        */
     LLAMA_KERNEL_ATTENTION = 2,  /* causal GQA attention (prefill or decode)           */
-    LLAMA_KERNEL_WO = 3,         /* output projection with residual add               */
+    LLAMA_KERNEL_WO = 3,         /* output projection with residual add (or split-K
+                                    sums that the next RMSNorm adds)                  */
     LLAMA_KERNEL_FFN_UP = 4,     /* W1/W3 projection with SiLU * up                   */
-    LLAMA_KERNEL_FFN_DOWN = 5,   /* W2 projection with residual add                   */
+    LLAMA_KERNEL_FFN_DOWN = 5,   /* W2 projection with residual add (or split-K sums
+                                    that the next RMSNorm adds)                       */
     LLAMA_KERNEL_LM_HEAD = 6,    /* vocabulary projection                              */
     LLAMA_KERNEL_RMSNORM = 7     /* RMSNorm                                            */
 } llama_kernel;
